@@ -1,0 +1,186 @@
+/*
+ * moe.h - C ABI of libmoe_mi355x: the forward pass of one DeepSpeed-MoE-style
+ * mixture-of-experts FFN layer on one MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * The layer ("[Review] DeepSpeed-MoE", section "What is MoE?": a Switch-Transformer
+ * style layer in which a gating function sends each token to one of several expert
+ * FFNs; section "Phenomenon2": Top2-MoE adds the outputs of two experts, and
+ * Residual-MoE adds a fixed dense MLP to one routed expert):
+ *
+ *   z      = x Wg^T (+ b)                      gate logits, fp32           [T, E]
+ *   p      = softmax(z) over all E experts     fp32
+ *   idx    = top-k experts by z, ties to the lower expert index            [T, k]
+ *   w      = p[idx]   (optionally renormalised over the k selected)        [T, k]
+ *   C      = ceil(k * T * cf / E)              capacity per expert
+ *   dispatch: assignments in rank-major order (all first choices, then all
+ *            second choices; lower token first); an assignment keeps slot
+ *            pos < C of its expert, later ones are dropped (contribute 0)
+ *   FFN_e(r) = GeLU(r W1_e^T + b1_e) W2_e^T + b2_e,  GeLU exact (erf form)
+ *   y[t]   = sum_j w[t,j] FFN_{idx[t,j]}(x[t]) over kept local assignments
+ *            (+ MLP(x[t]) in residual mode, the PR-MoE variant)
+ *
+ * One GPU may hold a share of the experts: local experts [first_local_expert,
+ * first_local_expert + num_local_experts). Gate, softmax and capacity are always
+ * global; dispatch, FFN and combine cover local experts, so y is this share's
+ * partial output and the shares of all GPUs sum to the full layer.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host). The caller allocates and
+ *     owns every buffer, including the workspace; the library keeps no pointer
+ *     past the call, allocates nothing and never synchronises the stream.
+ *   - Calls enqueue on `stream` and return at once (stream order). No device data
+ *     is read on the host, so a sequence of calls can be captured in a hipGraph.
+ *   - Argument errors are found on the host before anything is enqueued; then
+ *     nothing is launched and the status says why (moe_last_error() holds detail,
+ *     per thread). A failed launch returns MOE_ERR_HIP.
+ *   - Outputs are fully overwritten (dropped / non-local rows included).
+ *   - Results are bit-identical from run to run (no floating-point atomics).
+ *   - Tensors are row-major; weights use the nn.Linear layout [out, in]. Device
+ *     pointers must be 16-byte aligned; hidden and ffn must be multiples of 64.
+ *   - T == 0 is a valid no-op.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, k not in {1,2}, k > E, cf <= 0, ... */
+  MOE_ERR_UNSUPPORTED = 2,        /* valid layer the kernels do not cover (H % 64 != 0, ...) */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP launch or runtime call failed */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_F16 = 1, MOE_DTYPE_BF16 = 2 } moe_dtype_t;
+
+/* "DeepSpeed-MoE Inference" wiki page, section on PR-MoE: the model type is
+ * 'standard' or 'residual'; residual adds a dense MLP to one routed expert. */
+typedef enum { MOE_MLP_STANDARD = 0, MOE_MLP_RESIDUAL = 1 } moe_mlp_type_t;
+
+/* Divide the k combine weights of a token by their sum (before drops). Off by
+ * default: the combine weight is the raw softmax probability of the expert. */
+#define MOE_FLAG_RENORM_TOPK 1u
+
+typedef struct {
+  int64_t num_tokens;          /* T >= 0 */
+  int32_t hidden;              /* H, multiple of 64 */
+  int32_t ffn;                 /* F (expert and dense-MLP width), multiple of 64 */
+  int32_t num_experts;         /* E >= 1: gate width and capacity denominator, <= 1024 */
+  int32_t first_local_expert;  /* e_lo, 0 <= e_lo < E */
+  int32_t num_local_experts;   /* E_loc >= 1, e_lo + E_loc <= E */
+  int32_t top_k;               /* 1 or 2, <= E */
+  double capacity_factor;      /* finite and > 0 */
+  moe_mlp_type_t mlp_type;     /* RESIDUAL requires top_k == 1 */
+  moe_dtype_t dtype;           /* activations, weights and output; accumulation is fp32 */
+  uint32_t flags;              /* MOE_FLAG_* */
+} moe_layer_desc_t;
+
+typedef struct {
+  const void* gate_w;          /* [E, H] dtype */
+  const float* gate_b;         /* [E] fp32, or NULL for no gate bias */
+  const void* w1;              /* [E_loc, F, H] dtype */
+  const void* b1;              /* [E_loc, F]    dtype */
+  const void* w2;              /* [E_loc, H, F] dtype */
+  const void* b2;              /* [E_loc, H]    dtype */
+  const void* mlp_w1;          /* residual only: [F, H]; else ignored (may be NULL) */
+  const void* mlp_b1;          /* residual only: [F] */
+  const void* mlp_w2;          /* residual only: [H, F] */
+  const void* mlp_b2;          /* residual only: [H] */
+} moe_layer_weights_t;
+
+/* Capacity C = ceil(k * T * cf / E) (host, pure). The pages print no formula;
+ * this is the plainest reading, with the global expert count and no floor.
+ * Returns -1 for invalid arguments. */
+int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double cf);
+
+/* R_max = min(E_loc * C, k * T): rows of the dispatched buffers (host, pure).
+ * Returns -1 if the descriptor is invalid. */
+int64_t moe_max_rows(const moe_layer_desc_t* d);
+
+/* Workspace bytes that moe_layer_forward needs for this descriptor (host). Also
+ * enough for every step entry point below. */
+moe_status_t moe_workspace_size(const moe_layer_desc_t* d, size_t* bytes /* host */);
+
+/* Gate (steps z, p, idx, w above): x [T, H] dtype -> topk_idx [T, k] int32,
+ * topk_w [T, k] fp32, and, when probs != NULL, probs [T, E] fp32. Logits,
+ * softmax and the top-k choice are computed in fp32; ties go to the lower index.
+ * Softmax-based routing: "Fast MoE Inference via Predictive Prefetching and
+ * Expert Replication", problem statement. */
+moe_status_t moe_gate(const moe_layer_desc_t* d, const void* x, const void* gate_w,
+                      const float* gate_b, int32_t* topk_idx, float* topk_w, float* probs,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch (capacity and rank-major drops), atomic-free: per-block counts,
+ * column scan, stable in-block ranks. From topk_idx [T, k] int32 (values in
+ * [0, E)) writes:
+ *   expert_demand  [E]        assignments per global expert (all, kept or not)
+ *   expert_offsets [E_loc+1]  exclusive scan of kept rows per local expert
+ *   slot_token     [R_max]    token of each dispatched row, -1 past the last row
+ *   token_slot     [T, k]     row of each assignment, -1 if dropped or non-local
+ *   x_disp         [R_max, H] dtype, gathered x rows (zero past the last row)
+ * x_disp may be NULL to skip the gather. */
+moe_status_t moe_dispatch(const moe_layer_desc_t* d, const int32_t* topk_idx, const void* x,
+                          int32_t* expert_demand, int32_t* expert_offsets, int32_t* slot_token,
+                          int32_t* token_slot, void* x_disp, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Expert FFN over the dispatched rows, grouped by local expert:
+ * y_disp[r] = GeLU(x_disp[r] W1_e^T + b1_e) W2_e^T + b2_e for r in segment e
+ * ([expert_offsets[e], expert_offsets[e+1])). The hidden activation is rounded to
+ * dtype; accumulation is fp32; y_disp [R_max, H] is fp32 (rows past the last
+ * dispatched row are left unspecified). "[Review] DeepSpeed-MoE", "What is MoE?":
+ * the experts are FFNs; the page's model table fixes F = 4H for its models. */
+moe_status_t moe_expert_ffn(const moe_layer_desc_t* d, const void* x_disp,
+                            const int32_t* expert_offsets, const moe_layer_weights_t* w,
+                            float* y_disp, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dense MLP of the residual (PR-MoE) variant over all T tokens:
+ * out [T, H] fp32 = GeLU(x W1^T + b1) W2^T + b2 with the mlp_* weights.
+ * ("[Review] DeepSpeed-MoE", "Phenomenon2": Residual-MoE keeps a fixed MLP.) */
+moe_status_t moe_dense_ffn(const moe_layer_desc_t* d, const void* x, const moe_layer_weights_t* w,
+                           float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine: y[t] = sum over j with token_slot[t,j] >= 0 of topk_w[t,j] * y_disp[token_slot[t,j]]
+ * (+ dense_out[t] when dense_out != NULL), summed in fp32 in choice order and
+ * rounded once to dtype. y [T, H] is fully written. */
+moe_status_t moe_combine(const moe_layer_desc_t* d, const float* y_disp, const int32_t* token_slot,
+                         const float* topk_w, const float* dense_out, void* y, hipStream_t stream);
+
+/* The whole layer: x [T, H] dtype -> y [T, H] dtype, using ws of at least
+ * moe_workspace_size() bytes. In residual mode the dense MLP runs too. */
+moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const moe_layer_weights_t* w,
+                               const void* x, void* y, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* Optional timing hook for moe_layer_forward_ex: any non-NULL event is recorded on
+ * the stream right before / after the phase (gate, dispatch, expert FFN, combine). */
+typedef struct {
+  hipEvent_t gate_begin, gate_end;
+  hipEvent_t dispatch_begin, dispatch_end;
+  hipEvent_t ffn_begin, ffn_end;
+  hipEvent_t combine_begin, combine_end;
+} moe_phase_events_t;
+
+/* moe_layer_forward with phase events (ev may be NULL: then identical to it). */
+moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_weights_t* w,
+                                  const void* x, void* y, void* ws, size_t ws_bytes,
+                                  hipStream_t stream, const moe_phase_events_t* ev);
+
+/* Static text for a status code. */
+const char* moe_status_str(moe_status_t st);
+
+/* Detail of the last error on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

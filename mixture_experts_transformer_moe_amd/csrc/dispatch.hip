@@ -1,0 +1,297 @@
+// Dispatch: capacity-limited, rank-major, atomic-free assignment of tokens to
+// per-expert segments.
+//
+// Assignment a = j * T + t (choice j of token t) is ranked before every
+// assignment with a larger a, so all first choices outrank all second choices
+// and lower tokens outrank higher ones. pos(a) = number of earlier assignments
+// to the same expert; the assignment keeps row offsets[e] + pos(a) of its local
+// expert while pos(a) < C and is dropped otherwise.
+//
+// No atomics anywhere: inside a wave, lanes with the same expert find each other
+// with one ballot per key bit; waves are combined by a per-expert scan in LDS;
+// blocks by a per-expert scan over the blocks' histograms.
+#include "common.h"
+#include "kernels.h"
+#include "topk.h"
+
+namespace moe {
+
+#define DISP_BLOCK 1024
+#define DISP_WAVES (DISP_BLOCK / MOE_WAVE)
+
+// Mask of the lanes whose key equals this lane's key (all 64 lanes active).
+__device__ inline uint64_t match_lanes(int key, int nbits) {
+  uint64_t m = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const int bit = (key >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+__device__ inline int key_bits(int E) { return 32 - __clz(E); }   // keys 0..E fit
+
+// Block-level stable ranking of DISP_BLOCK keys in [0, E] (E = "no expert").
+// On return: wcnt[w * (E+1) + e] holds the number of keys e in waves < w of this
+// block, *tot (per expert, E entries) the block's count, and the return value
+// is the rank of this thread's key among equal keys of lower threads.
+__device__ inline int block_rank(int key, int E, int* wcnt, int* tot) {
+  const int tid = threadIdx.x;
+  const int w = tid / MOE_WAVE;
+  const int lane = lane_id();
+  const int stride = E + 1;
+  for (int i = tid; i < DISP_WAVES * stride; i += DISP_BLOCK) wcnt[i] = 0;
+  __syncthreads();
+  const uint64_t m = match_lanes(key, key_bits(E));
+  const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+  const int rank_w = __popcll(below);
+  if (rank_w == 0) wcnt[w * stride + key] = __popcll(m);
+  __syncthreads();
+  for (int e = tid; e < E; e += DISP_BLOCK) {
+    int run = 0;
+    for (int ww = 0; ww < DISP_WAVES; ++ww) {
+      const int c = wcnt[ww * stride + e];
+      wcnt[ww * stride + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  return (key < E) ? wcnt[w * stride + key] + rank_w : -1;
+}
+
+// Exclusive scan of one int per thread over the whole block (DISP_BLOCK threads).
+__device__ inline int block_excl_scan(int v, int* sh /* DISP_WAVES + 1 ints */, int* total) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / MOE_WAVE;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < MOE_WAVE; o <<= 1) {
+    int u = __shfl_up(incl, o, MOE_WAVE);
+    if (lane >= o) incl += u;
+  }
+  if (lane == MOE_WAVE - 1) sh[w] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < DISP_WAVES; ++i) { int c = sh[i]; sh[i] = run; run += c; }
+    sh[DISP_WAVES] = run;
+  }
+  __syncthreads();
+  const int r = sh[w] + incl - v;
+  *total = sh[DISP_WAVES];
+  __syncthreads();
+  return r;
+}
+
+__device__ inline int load_key(const int* idx, int a, int T, int k, int E) {
+  const int j = a / T;
+  const int t = a - j * T;
+  const int e = idx[(long long)t * k + j];
+  return (e >= 0 && e < E) ? e : E;
+}
+
+// -------------------------------------------------------------------- multi-block path
+__global__ __launch_bounds__(DISP_BLOCK) void dispatch_count_kernel(const int* __restrict__ idx, int T,
+                                                                    int k, int E, int* __restrict__ rank,
+                                                                    int* __restrict__ blk_hist) {
+  extern __shared__ int sh[];
+  int* wcnt = sh;                                  // DISP_WAVES * (E + 1)
+  int* tot = sh + DISP_WAVES * (E + 1);            // E
+  const int kT = T * k;
+  const int a = blockIdx.x * DISP_BLOCK + threadIdx.x;
+  const int key = (a < kT) ? load_key(idx, a, T, k, E) : E;
+  const int r = block_rank(key, E, wcnt, tot);
+  for (int e = threadIdx.x; e < E; e += DISP_BLOCK) blk_hist[(long long)blockIdx.x * E + e] = tot[e];
+  if (a < kT) rank[a] = r;
+}
+
+// Column scan of the block histograms (becomes each block's per-expert base),
+// demand, kept rows and the local segment offsets. One block.
+__global__ __launch_bounds__(DISP_BLOCK) void dispatch_scan_kernel(int* __restrict__ blk_hist, int nblk,
+                                                                   int E, int e_lo, int E_loc, int C,
+                                                                   int* __restrict__ demand,
+                                                                   int* __restrict__ offsets) {
+  __shared__ int sdem[1024];
+  __shared__ int ssc[DISP_WAVES + 1];
+  const int tid = threadIdx.x;
+  if (tid < E) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk_hist[(long long)b * E + tid];
+      blk_hist[(long long)b * E + tid] = run;
+      run += c;
+    }
+    demand[tid] = run;
+    sdem[tid] = run;
+  }
+  __syncthreads();
+  const int kept = (tid < E_loc) ? min(sdem[e_lo + tid], C) : 0;
+  int total;
+  const int off = block_excl_scan(kept, ssc, &total);
+  if (tid < E_loc) offsets[tid] = off;
+  if (tid == 0) offsets[E_loc] = total;
+}
+
+__global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
+    const int* __restrict__ idx, const int* __restrict__ rank, const int* __restrict__ base, int T, int k,
+    int E, int e_lo, int E_loc, int C, const int* __restrict__ offsets, int R_max,
+    int* __restrict__ slot_token, int* __restrict__ token_slot) {
+  const int kT = T * k;
+  const int a = blockIdx.x * DISP_BLOCK + threadIdx.x;
+  if (a < kT) {
+    const int j = a / T;
+    const int t = a - j * T;
+    const int e = load_key(idx, a, T, k, E);
+    int slot = -1;
+    if (e < E && e >= e_lo && e < e_lo + E_loc) {
+      const int pos = base[(long long)blockIdx.x * E + e] + rank[a];
+      if (pos < C) {
+        slot = offsets[e - e_lo] + pos;
+        slot_token[slot] = t;
+      }
+    }
+    token_slot[(long long)t * k + j] = slot;
+  }
+  const int R = offsets[E_loc];
+  for (int s = R + blockIdx.x * DISP_BLOCK + threadIdx.x; s < R_max; s += gridDim.x * DISP_BLOCK)
+    slot_token[s] = -1;
+}
+
+// -------------------------------------------------------------------- one-block path
+// Whole dispatch for k*T <= DISP_BLOCK in one launch; with FUSE_TOPK it first
+// runs the softmax / top-k of every token from the logits z (one wave per token).
+template <bool FUSE_TOPK>
+__global__ __launch_bounds__(DISP_BLOCK) void dispatch_small_kernel(
+    const float* z, int renorm, float* probs, float* __restrict__ topk_w, int* idx, int T, int k, int E,
+    int e_lo, int E_loc, int C, int R_max, int* __restrict__ demand, int* __restrict__ offsets,
+    int* __restrict__ slot_token, int* __restrict__ token_slot) {
+  extern __shared__ int sh[];
+  int* wcnt = sh;                                   // DISP_WAVES * (E + 1)
+  int* tot = wcnt + DISP_WAVES * (E + 1);           // E
+  int* sidx = tot + E;                              // DISP_BLOCK
+  int* ssc = sidx + DISP_BLOCK;                     // DISP_WAVES + 1
+  const int tid = threadIdx.x;
+  const int kT = T * k;
+  if (FUSE_TOPK) {
+    const int w = tid / MOE_WAVE;
+    for (int t = w; t < T; t += DISP_WAVES) {
+      int sel[2];
+      wave_softmax_topk(z + (long long)t * E, E, k, renorm != 0, probs ? probs + (long long)t * E : nullptr,
+                        idx + (long long)t * k, topk_w + (long long)t * k, sel);
+      if (lane_id() == 0)
+        for (int j = 0; j < k; ++j) sidx[j * T + t] = sel[j];
+    }
+    __syncthreads();
+  }
+  int key = E;
+  if (tid < kT) {
+    if (FUSE_TOPK) {
+      const int e = sidx[tid];
+      key = (e >= 0 && e < E) ? e : E;
+    } else {
+      key = load_key(idx, tid, T, k, E);
+    }
+  }
+  const int r = block_rank(key, E, wcnt, tot);
+  for (int e = tid; e < E; e += DISP_BLOCK) demand[e] = tot[e];
+  const int kept = (tid < E_loc) ? min(tot[e_lo + tid], C) : 0;
+  int total;
+  const int off = block_excl_scan(kept, ssc, &total);
+  if (tid < E_loc) sidx[tid] = off;   // reuse: segment offsets (the keys are already in registers)
+  if (tid < E_loc) offsets[tid] = off;
+  if (tid == 0) offsets[E_loc] = total;
+  __syncthreads();
+  if (tid < kT) {
+    const int j = tid / T;
+    const int t = tid - j * T;
+    int slot = -1;
+    if (key < E && key >= e_lo && key < e_lo + E_loc && r < C) {
+      slot = sidx[key - e_lo] + r;
+      slot_token[slot] = t;
+    }
+    token_slot[(long long)t * k + j] = slot;
+  }
+  for (int s = total + tid; s < R_max; s += DISP_BLOCK) slot_token[s] = -1;
+}
+
+// Gather x rows into the dispatched order (zero rows past the last one).
+template <typename DT>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const typename DT::T* __restrict__ x,
+                                                          const int* __restrict__ slot_token, int H,
+                                                          typename DT::T* __restrict__ xd) {
+  const int s = blockIdx.x;
+  const int t = slot_token[s];
+  const int nvec = H / DT::VEC;
+  uint4* dst = reinterpret_cast<uint4*>(xd + (long long)s * H);
+  if (t >= 0) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (long long)t * H);
+    for (int c = threadIdx.x; c < nvec; c += 256) dst[c] = src[c];
+  } else {
+    for (int c = threadIdx.x; c < nvec; c += 256) dst[c] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// -------------------------------------------------------------------- launchers
+size_t dispatch_small_lds(int E) {
+  return sizeof(int) * ((size_t)DISP_WAVES * (E + 1) + E + DISP_BLOCK + DISP_WAVES + 1);
+}
+
+hipError_t launch_dispatch_small(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w,
+                                 int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
+                                 int* demand, int* offsets, int* slot_token, int* token_slot,
+                                 hipStream_t s) {
+  const size_t lds = dispatch_small_lds(E);
+  if (fuse_topk)
+    hipLaunchKernelGGL(dispatch_small_kernel<true>, dim3(1), dim3(DISP_BLOCK), lds, s, z, renorm, probs,
+                       topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token,
+                       token_slot);
+  else
+    hipLaunchKernelGGL(dispatch_small_kernel<false>, dim3(1), dim3(DISP_BLOCK), lds, s, z, renorm, probs,
+                       topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token,
+                       token_slot);
+  return hipGetLastError();
+}
+
+int dispatch_num_blocks(long long kT) { return (int)((kT + DISP_BLOCK - 1) / DISP_BLOCK); }
+int dispatch_block_size() { return DISP_BLOCK; }
+
+hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
+                                 int* rank, int* blk_hist, int* demand, int* offsets, int* slot_token,
+                                 int* token_slot, hipStream_t s) {
+  const int nblk = dispatch_num_blocks((long long)T * k);
+  const size_t lds = sizeof(int) * ((size_t)DISP_WAVES * (E + 1) + E);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(DISP_BLOCK), lds, s, idx, T, k, E, rank,
+                     blk_hist);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(DISP_BLOCK), 0, s, blk_hist, nblk, E, e_lo, E_loc,
+                     C, demand, offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(DISP_BLOCK), 0, s, idx, rank, blk_hist, T, k,
+                     E, e_lo, E_loc, C, offsets, R_max, slot_token, token_slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(int dtype, const void* x, const int* slot_token, int R_max, int H, void* xd,
+                              hipStream_t s) {
+  if (R_max <= 0) return hipSuccess;
+  switch (dtype) {
+    case DT_F32:
+      hipLaunchKernelGGL(gather_rows_kernel<DtF32>, dim3(R_max), dim3(256), 0, s, (const float*)x, slot_token,
+                         H, (float*)xd);
+      break;
+    case DT_F16:
+      hipLaunchKernelGGL(gather_rows_kernel<DtF16>, dim3(R_max), dim3(256), 0, s, (const _Float16*)x,
+                         slot_token, H, (_Float16*)xd);
+      break;
+    default:
+      hipLaunchKernelGGL(gather_rows_kernel<DtBF16>, dim3(R_max), dim3(256), 0, s, (const __bf16*)x,
+                         slot_token, H, (__bf16*)xd);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,344 @@
+// Grouped GEMM over variable-length expert segments on the CDNA4 matrix cores.
+//
+//   C[r, n] = epi( sum_k A[arow(r), k] * B_s[n, k] + bias_s[n] )   for r in segment s
+//
+// Both operands are K-contiguous (nn.Linear weights, row-major activations), so
+// every lane moves 16-byte vectors along K. The MFMA "A" operand is the weight
+// tile (its rows become output columns n) and the "B" operand the activation
+// tile (rows m), so each lane of a 16x16 accumulator holds four consecutive n of
+// one output row: the epilogue stores 4 contiguous values per lane.
+//
+// A work-group computes a BM x BN output tile with 4 waves; K advances 128 bytes
+// per stage through double-buffered LDS (row pitch 144 B: the 16 lanes of a
+// quarter-wave read 16 rows at distinct banks). Epilogues: bias + exact GeLU
+// rounded to the I/O dtype (first expert GEMM), or bias in fp32 (second GEMM
+// and gate logits).
+//
+// Tiles come from a device tile list built by the plan kernel from the segment
+// offsets (no host sync): order is segment, then column tile, then m-tile, so
+// the m-tiles that share a weight tile are adjacent; the block index is remapped
+// so adjacent tiles land on the same XCD (work-groups are dealt round-robin over
+// the 8 XCDs) and share its L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+#define GEMM_THREADS 256
+#define LDS_ROW 144      // bytes per LDS row: 128 bytes of K + 16 pad
+
+template <typename DT>
+struct Mfma;
+
+template <>
+struct Mfma<DtF16> {
+  __device__ static inline float4_t op(const uint4& a, const uint4& b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
+                                                   c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<DtBF16> {
+  __device__ static inline float4_t op(const uint4& a, const uint4& b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<DtF32> {
+  // four K=4 steps; element i of every lane's vector is the same K position
+  // for both operands, so the products pair up correctly
+  __device__ static inline float4_t op(const uint4& a, const uint4& b, float4_t c) {
+    const float4 fa = __builtin_bit_cast(float4, a);
+    const float4 fb = __builtin_bit_cast(float4, b);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, fb.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, fb.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, fb.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, fb.w, c, 0, 0, 0);
+    return c;
+  }
+};
+
+// Bijection on [0, total) placing consecutive tiles on one XCD.
+__device__ inline int xcd_remap(int i, int total) {
+  const int NX = 8;
+  const int xcd = i % NX, slot = i / NX;
+  const int q = total / NX, r = total % NX;
+  return xcd * q + min(xcd, r) + slot;
+}
+
+template <typename BiasT>
+__device__ inline float load_bias(const BiasT* b, int n);
+template <>
+__device__ inline float load_bias<float>(const float* b, int n) { return b[n]; }
+template <>
+__device__ inline float load_bias<_Float16>(const _Float16* b, int n) { return (float)b[n]; }
+template <>
+__device__ inline float load_bias<__bf16>(const __bf16* b, int n) { return (float)b[n]; }
+
+template <typename DT, int BM, int BN, int EPI, typename BiasT>
+__global__ __launch_bounds__(GEMM_THREADS) void grouped_gemm_kernel(GemmParams p) {
+  using T = typename DT::T;
+  constexpr int WM = (BM >= 64) ? 2 : 1;
+  constexpr int WN = 4 / WM;
+  constexpr int TN = BN / WN / 16;
+  constexpr int TM = BM / WM / 16;
+  static_assert(TN >= 1 && TM >= 1, "tile too small for 4 waves");
+  constexpr int ACH = (BM * 8 + GEMM_THREADS - 1) / GEMM_THREADS;   // 16-byte chunks per thread
+  constexpr int BCH = (BN * 8) / GEMM_THREADS;
+  static_assert(BCH >= 1, "BN too small");
+  constexpr int STAGE = (BN + BM) * LDS_ROW;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  // ---- which tile
+  int nmt;
+  if (p.tiles) nmt = *p.tile_count;
+  else nmt = (p.M + BM - 1) / BM;
+  const int total = nmt * p.n_ntiles;
+  if ((int)blockIdx.x >= total) return;
+  const int L = xcd_remap(blockIdx.x, total);
+  int seg, nt, mt, r0, r1;
+  if (p.tiles) {
+    const int2 d = p.tiles[L];
+    seg = d.x;
+    nt = d.y >> 16;
+    mt = d.y & 0xffff;
+    r0 = p.seg_off[seg];
+    r1 = p.seg_off[seg + 1];
+  } else {
+    seg = 0;
+    nt = L / nmt;
+    mt = L - nt * nmt;
+    r0 = 0;
+    r1 = p.M;
+  }
+  const int m0 = r0 + mt * BM;        // first row-space row of the tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_n = wave % WN;
+  const int wave_m = wave / WN;
+
+  // ---- per-thread global source rows
+  const char* a_src[ACH];
+  int a_dst[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int c = tid + i * GEMM_THREADS;
+    const int row = c >> 3, col = c & 7;
+    int r = m0 + row;
+    if (r >= r1) r = r1 - 1;
+    const long long arow = p.a_rows ? (long long)p.a_rows[r] : (long long)r;
+    a_src[i] = (c < BM * 8) ? reinterpret_cast<const char*>(p.A) + (arow * p.K) * (long long)sizeof(T) + col * 16
+                            : nullptr;
+    a_dst[i] = BN * LDS_ROW + row * LDS_ROW + col * 16;
+  }
+  const char* b_src[BCH];
+  int b_dst[BCH];
+  const char* bbase = reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int c = tid + i * GEMM_THREADS;
+    const int row = c >> 3, col = c & 7;
+    const long long n = (long long)nt * BN + row;
+    b_src[i] = bbase + n * p.K * (long long)sizeof(T) + col * 16;
+    b_dst[i] = row * LDS_ROW + col * 16;
+  }
+
+  float4_t acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[ACH], rb[BCH];
+  const int nk = (int)(((long long)p.K * sizeof(T)) / 128);
+
+  auto gload = [&](int ks) {
+    const long long off = (long long)ks * 128;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+      if (a_src[i]) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + off);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + off);
+  };
+  auto lstore = [&](int buf) {
+    char* base = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+      if (a_src[i]) *reinterpret_cast<uint4*>(base + a_dst[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) *reinterpret_cast<uint4*>(base + b_dst[i]) = rb[i];
+  };
+
+  const int frag_row = lane & 15;
+  const int frag_k = (lane >> 4) * 16;   // byte offset within a 64-byte k-block
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) gload(ks + 1);
+    const char* sb = smem + buf * STAGE;
+    const char* sa = sb + BN * LDS_ROW;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint4 fa[TN], fb[TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        fa[i] = *reinterpret_cast<const uint4*>(sb + (wave_n * TN * 16 + i * 16 + frag_row) * LDS_ROW +
+                                                kb * 64 + frag_k);
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        fb[j] = *reinterpret_cast<const uint4*>(sa + (wave_m * TM * 16 + j * 16 + frag_row) * LDS_ROW +
+                                                kb * 64 + frag_k);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = Mfma<DT>::op(fa[i], fb[j], acc[i][j]);
+    }
+    if (ks + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds D[n = 4*(lane/16) + q][m = lane % 16], q = 0..3
+  const BiasT* bias = p.bias ? reinterpret_cast<const BiasT*>(p.bias) + (long long)seg * p.bias_stride : nullptr;
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    const int n = nt * BN + wave_n * TN * 16 + i * 16 + (lane >> 4) * 4;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bv[q] = load_bias<BiasT>(bias, n + q);
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int r = m0 + wave_m * TM * 16 + j * 16 + (lane & 15);
+      if (r >= r1) continue;
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] + bv[q];
+      if constexpr (EPI == EPI_GELU) {
+        T o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = DT::from_f(gelu_erf(v[q]));
+        T* dst = reinterpret_cast<T*>(p.C) + (long long)r * p.N + n;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[q] = o[q];
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(p.C) + (long long)r * p.N + n;
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- plan kernel
+__global__ __launch_bounds__(1024) void gemm_plan_kernel(const int* __restrict__ seg_off, int nseg, int BM,
+                                                        int n_nt1, int n_nt2, int2* __restrict__ list1,
+                                                        int2* __restrict__ list2, int* __restrict__ count) {
+  __shared__ int P[1025];
+  __shared__ int C[1024];
+  __shared__ int wsum[17];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int c = (tid < nseg) ? (seg_off[tid + 1] - seg_off[tid] + BM - 1) / BM : 0;
+  C[tid] = c;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 16; ++i) { const int t = wsum[i]; wsum[i] = run; run += t; }
+    wsum[16] = run;
+  }
+  __syncthreads();
+  P[tid] = wsum[w] + incl - c;
+  if (tid == 0) P[nseg] = wsum[16];
+  __syncthreads();
+  const int total = wsum[16];
+  if (tid == 0) count[0] = total;
+  for (int g = 0; g < 2; ++g) {
+    const int n_nt = g ? n_nt2 : n_nt1;
+    int2* list = g ? list2 : list1;
+    if (!list) continue;
+    for (int L = tid; L < total * n_nt; L += 1024) {
+      const int v = L / n_nt;
+      int lo = 0, hi = nseg;               // largest s with P[s] <= v and P[s+1] > v
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (P[mid] <= v) lo = mid; else hi = mid;
+      }
+      const int s = lo;
+      const int q = L - P[s] * n_nt;
+      const int cs = C[s];
+      const int nt = q / cs, mt = q - (q / cs) * cs;
+      list[L] = make_int2(s, (nt << 16) | mt);
+    }
+  }
+}
+
+hipError_t launch_gemm_plan(const int* seg_off, int nseg, int BM, int n_nt1, int n_nt2, int2* list1, int2* list2,
+                            int* count, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, seg_off, nseg, BM, n_nt1, n_nt2, list1, list2,
+                     count);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- dispatch on shape
+template <typename DT, int BM, int BN, int EPI, typename BiasT>
+static void launch_t(const GemmParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT>), dim3(grid), dim3(GEMM_THREADS), 0, s, p);
+}
+
+template <typename DT, int BM, int BN>
+static void launch_epi(int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s) {
+  using T = typename DT::T;
+  if (epi == EPI_GELU) launch_t<DT, BM, BN, EPI_GELU, T>(p, grid, s);
+  else if (bias_f32) launch_t<DT, BM, BN, EPI_F32, float>(p, grid, s);
+  else launch_t<DT, BM, BN, EPI_F32, T>(p, grid, s);
+}
+
+template <typename DT, int BN>
+static bool launch_bm(int BM, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s) {
+  switch (BM) {
+    case 16: launch_epi<DT, 16, BN>(epi, bias_f32, p, grid, s); return true;
+    case 32: launch_epi<DT, 32, BN>(epi, bias_f32, p, grid, s); return true;
+    case 64: launch_epi<DT, 64, BN>(epi, bias_f32, p, grid, s); return true;
+    case 128: launch_epi<DT, 128, BN>(epi, bias_f32, p, grid, s); return true;
+  }
+  return false;
+}
+
+template <typename DT>
+static bool launch_bn(int BM, int BN, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s) {
+  if (BN == 128) return launch_bm<DT, 128>(BM, epi, bias_f32, p, grid, s);
+  if (BN == 64) return launch_bm<DT, 64>(BM, epi, bias_f32, p, grid, s);
+  return false;
+}
+
+hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN, const GemmParams& p, int grid,
+                               hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  bool ok;
+  switch (dtype) {
+    case DT_F32: ok = launch_bn<DtF32>(BM, BN, epi, bias_f32, p, grid, s); break;
+    case DT_F16: ok = launch_bn<DtF16>(BM, BN, epi, bias_f32, p, grid, s); break;
+    default: ok = launch_bn<DtBF16>(BM, BN, epi, bias_f32, p, grid, s); break;
+  }
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,53 @@
+// Host-side launchers of the HIP kernels (one definition per kernel file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "common.h"
+
+namespace moe {
+
+// gate.hip
+hipError_t launch_gate_logits_fma(int dtype, const void* x, const void* wg, const float* bias, float* z,
+                                  int T, int H, int E, hipStream_t s);
+hipError_t launch_softmax_topk(const float* z, int T, int E, int k, int renorm, int* idx, float* w,
+                               float* probs, hipStream_t s);
+
+// dispatch.hip
+size_t dispatch_small_lds(int E);
+int dispatch_num_blocks(long long kT);
+int dispatch_block_size();
+hipError_t launch_dispatch_small(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w,
+                                 int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
+                                 int* demand, int* offsets, int* slot_token, int* token_slot,
+                                 hipStream_t s);
+hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
+                                 int* rank, int* blk_hist, int* demand, int* offsets, int* slot_token,
+                                 int* token_slot, hipStream_t s);
+hipError_t launch_gather_rows(int dtype, const void* x, const int* slot_token, int R_max, int H, void* xd,
+                              hipStream_t s);
+
+// gemm.hip
+enum { EPI_GELU = 0, EPI_F32 = 1 };
+// Tile list for segments [seg_off[s], seg_off[s+1]) with BM-row m-tiles, for two
+// GEMMs with n_nt1 / n_nt2 column tiles. count[0] = number of m-tiles.
+hipError_t launch_gemm_plan(const int* seg_off, int nseg, int BM, int n_nt1, int n_nt2, int2* list1,
+                            int2* list2, int* count, hipStream_t s);
+// bias_f32 selects a float bias (gate) instead of a dtype bias.
+hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN, const GemmParams& p,
+                               int grid, hipStream_t s);
+
+// decode_ffn.hip
+constexpr int DECODE_BF = 64;
+size_t decode_ffn_lds(int dtype, int maxm, int H);
+hipError_t launch_decode_ffn(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(int dtype, const float* ysrc, int P, long long prow, const int* token_slot,
+                          const float* w, int k, const float* dense, int Pd, void* y, int T, int H,
+                          hipStream_t s);
+hipError_t launch_reduce_partials(const float* part, int P, long long prow, const int* offsets, int nseg,
+                                  int R_max, int H, float* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,610 @@
+// C ABI of the MoE layer library: argument checks, capacity, workspace layout
+// and the launch sequence. Everything here runs on the host; every step of the
+// layer itself runs in the kernels of the other files.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "moe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, where)                   \
+  do {                                         \
+    hipError_t _e = (expr);                    \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+constexpr int kMaxExperts = 512;
+constexpr size_t kAlign = 256;
+constexpr size_t kDecodeLdsMax = 48 * 1024;   // x rows staged in LDS by the decode kernel
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Exact ceil(k*T*cf / E) for a finite cf > 0 (cf = mant * 2^e2 exactly).
+int64_t capacity_exact(int64_t T, int32_t E, int32_t k, double cf) {
+  if (T == 0) return 0;
+  int ex;
+  const double f = frexp(cf, &ex);                       // cf = f * 2^ex, f in [0.5, 1)
+  const unsigned long long mant = (unsigned long long)ldexp(f, 53);
+  const int e2 = ex - 53;
+  const __int128 N = (__int128)T * k;
+  __int128 A = N * (__int128)mant;                       // < 2^32 * 2^53
+  if (e2 >= 0) {
+    if (e2 > 40) return INT64_MAX;
+    A <<= e2;
+    const __int128 q = (A + E - 1) / E;
+    return q > (__int128)INT64_MAX ? INT64_MAX : (int64_t)q;
+  }
+  const int s = -e2;
+  if (s + 11 >= 126) return A > 0 ? 1 : 0;               // E * 2^s exceeds A
+  const __int128 B = (__int128)E << s;
+  const __int128 q = (A + B - 1) / B;
+  return (int64_t)q;
+}
+
+int pow2_at_least(int64_t v) {
+  int m = 1;
+  while (m < v) m <<= 1;
+  return m;
+}
+
+int gemm_bm_for_rows(int64_t rows) {
+  if (rows <= 16) return 16;
+  if (rows <= 32) return 32;
+  if (rows <= 64) return 64;
+  return 128;
+}
+
+struct Plan {
+  int64_t T, C, R_max;
+  int H, F, E, e_lo, E_loc, k;
+  int dtype;
+  size_t esz;
+  bool residual, renorm;
+  // gate
+  bool gate_mfma;
+  int gate_BM, gate_BN;
+  // dispatch
+  bool disp_small;
+  int nblk;
+  // experts
+  bool exp_decode;
+  int exp_maxm;
+  int BM, BN1, BN2, mt_bound;
+  int P;  // decode slices
+  // dense MLP
+  bool dense_decode;
+  int dense_maxm, dBM, dBN1, dBN2;
+  // workspace offsets (bytes)
+  size_t o_z, o_idx, o_w, o_rank, o_blk, o_demand, o_off, o_slot_token, o_token_slot;
+  size_t o_part, o_h, o_ydisp, o_list1, o_list2, o_count;
+  size_t o_dpart, o_dh, o_dense;
+  size_t total;
+};
+
+moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
+  if (!d) return fail(MOE_ERR_INVALID_ARGUMENT, "descriptor is NULL");
+  if (d->num_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (d->hidden <= 0 || d->ffn <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "hidden and ffn must be > 0");
+  if (d->num_experts < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "num_experts must be >= 1");
+  if (d->top_k != 1 && d->top_k != 2) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k must be 1 or 2");
+  if (d->top_k > d->num_experts) return fail(MOE_ERR_INVALID_ARGUMENT, "top_k > num_experts");
+  if (d->first_local_expert < 0 || d->first_local_expert >= d->num_experts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "first_local_expert out of [0, E)");
+  if (d->num_local_experts < 1 || (int64_t)d->first_local_expert + d->num_local_experts > d->num_experts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "local expert range not inside [0, E)");
+  if (!(d->capacity_factor > 0.0) || !isfinite(d->capacity_factor))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "capacity_factor must be finite and > 0");
+  if (d->mlp_type != MOE_MLP_STANDARD && d->mlp_type != MOE_MLP_RESIDUAL)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown mlp_type");
+  if (d->mlp_type == MOE_MLP_RESIDUAL && d->top_k != 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "residual mode routes one expert per token (top_k must be 1)");
+  if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_F16 && d->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (d->flags & ~MOE_FLAG_RENORM_TOPK) return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flag bits");
+  if (d->hidden % 64 || d->ffn % 64) return fail(MOE_ERR_UNSUPPORTED, "hidden and ffn must be multiples of 64");
+  if (d->num_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "num_experts > %d", kMaxExperts);
+  if (d->num_tokens * (int64_t)d->top_k > (int64_t)(1 << 30))
+    return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k > 2^30");
+  if (d->ffn > (1 << 20) || d->hidden > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "hidden / ffn > 2^20");
+
+  Plan& p = *pl;
+  memset(&p, 0, sizeof(p));
+  p.T = d->num_tokens;
+  p.H = d->hidden;
+  p.F = d->ffn;
+  p.E = d->num_experts;
+  p.e_lo = d->first_local_expert;
+  p.E_loc = d->num_local_experts;
+  p.k = d->top_k;
+  p.dtype = (int)d->dtype;
+  p.esz = d->dtype == MOE_DTYPE_F32 ? 4 : 2;
+  p.residual = d->mlp_type == MOE_MLP_RESIDUAL;
+  p.renorm = (d->flags & MOE_FLAG_RENORM_TOPK) != 0;
+  p.C = capacity_exact(p.T, p.E, p.k, d->capacity_factor);
+  const int64_t kT = p.T * p.k;
+  p.R_max = (p.C >= kT) ? kT : std::min<int64_t>((int64_t)p.E_loc * p.C, kT);
+  if ((int64_t)p.R_max * std::max(p.H, p.F) > ((int64_t)1 << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "dispatched buffers too large");
+
+  // gate: matrix cores when the batch fills tiles, else one wave per expert
+  p.gate_mfma = p.T >= 64 && (p.E % 64) == 0;
+  p.gate_BM = 64;
+  p.gate_BN = (p.E % 128 == 0) ? 128 : 64;
+  // dispatch: one block when every assignment fits in it
+  p.disp_small = kT <= dispatch_block_size();
+  p.nblk = dispatch_num_blocks(kT);
+  // experts: fused streaming kernel for tiny segments, grouped MFMA GEMM otherwise
+  const int64_t seg_rows = std::min<int64_t>(p.C, kT);
+  p.exp_maxm = pow2_at_least(std::max<int64_t>(seg_rows, 1));
+  p.exp_decode = p.dtype != DT_F32 && seg_rows <= 8 && p.H % 512 == 0 &&
+                 decode_ffn_lds(p.dtype, p.exp_maxm, p.H) <= kDecodeLdsMax;
+  p.P = p.F / DECODE_BF;
+  p.BM = gemm_bm_for_rows(seg_rows);
+  p.BN1 = (p.F % 128 == 0) ? 128 : 64;
+  p.BN2 = (p.H % 128 == 0) ? 128 : 64;
+  {
+    const int64_t segs = std::min<int64_t>(p.E_loc, p.R_max);
+    const int64_t mtb = (p.R_max + (int64_t)(p.BM - 1) * segs) / p.BM;
+    if (!p.exp_decode && mtb >= 65536) return fail(MOE_ERR_UNSUPPORTED, "too many row tiles");
+    p.mt_bound = (int)mtb;
+    if (p.F / p.BN1 >= 65536 || p.H / p.BN2 >= 65536) return fail(MOE_ERR_UNSUPPORTED, "too many column tiles");
+  }
+  p.dense_maxm = pow2_at_least(std::max<int64_t>(p.T, 1));
+  p.dense_decode = p.dtype != DT_F32 && p.T <= 8 && p.H % 512 == 0 &&
+                   decode_ffn_lds(p.dtype, p.dense_maxm, p.H) <= kDecodeLdsMax;
+  p.dBM = gemm_bm_for_rows(p.T);
+  p.dBN1 = p.BN1;
+  p.dBN2 = p.BN2;
+
+  // workspace layout
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t T = (size_t)p.T, H = (size_t)p.H, F = (size_t)p.F, R = (size_t)p.R_max;
+  p.o_z = take(T * p.E * 4);
+  p.o_idx = take(T * p.k * 4);
+  p.o_w = take(T * p.k * 4);
+  p.o_rank = take(p.disp_small ? 0 : T * p.k * 4);
+  p.o_blk = take(p.disp_small ? 0 : (size_t)p.nblk * p.E * 4);
+  p.o_demand = take((size_t)p.E * 4);
+  p.o_off = take((size_t)(p.E_loc + 1) * 4);
+  p.o_slot_token = take(R * 4);
+  p.o_token_slot = take(T * p.k * 4);
+  if (p.exp_decode) {
+    p.o_part = take((size_t)p.P * R * H * 4);
+  } else {
+    p.o_h = take(R * F * p.esz);
+    p.o_ydisp = take(R * H * 4);
+    p.o_list1 = take((size_t)p.mt_bound * (F / p.BN1) * sizeof(int2));
+    p.o_list2 = take((size_t)p.mt_bound * (H / p.BN2) * sizeof(int2));
+    p.o_count = take(4);
+  }
+  if (p.residual) {
+    if (p.dense_decode) {
+      p.o_dpart = take((size_t)p.P * T * H * 4);
+    } else {
+      p.o_dh = take(T * F * p.esz);
+      p.o_dense = take(T * H * 4);
+    }
+  }
+  p.total = o;
+  return MOE_OK;
+}
+
+template <typename Tp>
+Tp* wsp(void* ws, size_t off) {
+  return reinterpret_cast<Tp*>(reinterpret_cast<char*>(ws) + off);
+}
+
+moe_status_t check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define PTR_TRY(p, name)                          \
+  do {                                            \
+    moe_status_t _s = check_ptr((p), (name));     \
+    if (_s != MOE_OK) return _s;                  \
+  } while (0)
+
+moe_status_t check_weights(const Plan& p, const moe_layer_weights_t* w, bool experts, bool dense) {
+  if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "weights is NULL");
+  if (experts) {
+    PTR_TRY(w->w1, "w1");
+    PTR_TRY(w->b1, "b1");
+    PTR_TRY(w->w2, "w2");
+    PTR_TRY(w->b2, "b2");
+  }
+  if (dense) {
+    PTR_TRY(w->mlp_w1, "mlp_w1");
+    PTR_TRY(w->mlp_b1, "mlp_b1");
+    PTR_TRY(w->mlp_w2, "mlp_w2");
+    PTR_TRY(w->mlp_b2, "mlp_b2");
+  }
+  (void)p;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- launch steps
+moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, const float* gate_b, float* z,
+                             hipStream_t s) {
+  if (p.gate_mfma) {
+    GemmParams g{};
+    g.A = x;
+    g.M = (int)p.T;
+    g.nseg = 1;
+    g.N = p.E;
+    g.K = p.H;
+    g.B = gate_w;
+    g.bias = gate_b;
+    g.C = z;
+    g.n_ntiles = p.E / p.gate_BN;
+    const int grid = (int)((p.T + p.gate_BM - 1) / p.gate_BM) * g.n_ntiles;
+    HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, true, p.gate_BM, p.gate_BN, g, grid, s), "gate logits (mfma)");
+  } else {
+    HIP_TRY(launch_gate_logits_fma(p.dtype, x, gate_w, gate_b, z, (int)p.T, p.H, p.E, s), "gate logits");
+  }
+  return MOE_OK;
+}
+
+moe_status_t run_dispatch(const Plan& p, bool fuse_topk, const float* z, float* probs, float* topk_w, int* idx,
+                          int* demand, int* offsets, int* slot_token, int* token_slot, void* ws, hipStream_t s) {
+  const int C = (int)std::min<int64_t>(p.C, INT32_MAX);
+  if (p.disp_small) {
+    HIP_TRY(launch_dispatch_small(fuse_topk, z, p.renorm ? 1 : 0, probs, topk_w, idx, (int)p.T, p.k, p.E, p.e_lo,
+                                  p.E_loc, C, (int)p.R_max, demand, offsets, slot_token, token_slot, s),
+            "dispatch (one block)");
+  } else {
+    if (fuse_topk)
+      HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, idx, topk_w, probs, s), "softmax/top-k");
+    HIP_TRY(launch_dispatch_multi(idx, (int)p.T, p.k, p.E, p.e_lo, p.E_loc, C, (int)p.R_max, wsp<int>(ws, p.o_rank),
+                                  wsp<int>(ws, p.o_blk), demand, offsets, slot_token, token_slot, s),
+            "dispatch");
+  }
+  return MOE_OK;
+}
+
+// Expert FFN. x rows come from x via slot_token (a_rows != null) or from
+// x_disp directly. Decode path leaves partials in ws; GEMM path writes ydisp.
+moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const int* offsets,
+                         const moe_layer_weights_t* w, float* ydisp, void* ws, hipStream_t s) {
+  if (p.exp_decode) {
+    DecodeParams d{};
+    d.x = x;
+    d.a_rows = a_rows;
+    d.seg_off = offsets;
+    d.nseg = p.E_loc;
+    d.H = p.H;
+    d.F = p.F;
+    d.w1 = w->w1;
+    d.b1 = w->b1;
+    d.w2 = w->w2;
+    d.b2 = w->b2;
+    d.part = wsp<float>(ws, p.o_part);
+    d.row_space = p.R_max;
+    const int gsegs = (int)std::min<int64_t>(p.E_loc, p.R_max);
+    HIP_TRY(launch_decode_ffn(p.dtype, p.exp_maxm, d, gsegs, s), "expert ffn (decode)");
+    return MOE_OK;
+  }
+  int2* l1 = wsp<int2>(ws, p.o_list1);
+  int2* l2 = wsp<int2>(ws, p.o_list2);
+  int* cnt = wsp<int>(ws, p.o_count);
+  const int nt1 = p.F / p.BN1, nt2 = p.H / p.BN2;
+  HIP_TRY(launch_gemm_plan(offsets, p.E_loc, p.BM, nt1, nt2, l1, l2, cnt, s), "gemm plan");
+  void* h = wsp<void>(ws, p.o_h);
+  GemmParams g1{};
+  g1.A = x;
+  g1.a_rows = a_rows;
+  g1.seg_off = offsets;
+  g1.nseg = p.E_loc;
+  g1.N = p.F;
+  g1.K = p.H;
+  g1.B = w->w1;
+  g1.b_stride = (long long)p.F * p.H;
+  g1.bias = w->b1;
+  g1.bias_stride = p.F;
+  g1.C = h;
+  g1.tiles = l1;
+  g1.tile_count = cnt;
+  g1.n_ntiles = nt1;
+  HIP_TRY(launch_grouped_gemm(p.dtype, EPI_GELU, false, p.BM, p.BN1, g1, p.mt_bound * nt1, s), "expert gemm 1");
+  GemmParams g2{};
+  g2.A = h;
+  g2.seg_off = offsets;
+  g2.nseg = p.E_loc;
+  g2.N = p.H;
+  g2.K = p.F;
+  g2.B = w->w2;
+  g2.b_stride = (long long)p.H * p.F;
+  g2.bias = w->b2;
+  g2.bias_stride = p.H;
+  g2.C = ydisp;
+  g2.tiles = l2;
+  g2.tile_count = cnt;
+  g2.n_ntiles = nt2;
+  HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, false, p.BM, p.BN2, g2, p.mt_bound * nt2, s), "expert gemm 2");
+  return MOE_OK;
+}
+
+// Dense MLP (residual mode). Decode path leaves partials at o_dpart; GEMM path writes out.
+moe_status_t run_dense(const Plan& p, const void* x, const moe_layer_weights_t* w, float* out, void* ws,
+                       hipStream_t s) {
+  if (p.dense_decode) {
+    DecodeParams d{};
+    d.x = x;
+    d.M = (int)p.T;
+    d.nseg = 1;
+    d.H = p.H;
+    d.F = p.F;
+    d.w1 = w->mlp_w1;
+    d.b1 = w->mlp_b1;
+    d.w2 = w->mlp_w2;
+    d.b2 = w->mlp_b2;
+    d.part = wsp<float>(ws, p.o_dpart);
+    d.row_space = p.T;
+    HIP_TRY(launch_decode_ffn(p.dtype, p.dense_maxm, d, 1, s), "dense mlp (decode)");
+    return MOE_OK;
+  }
+  void* h = wsp<void>(ws, p.o_dh);
+  GemmParams g1{};
+  g1.A = x;
+  g1.M = (int)p.T;
+  g1.nseg = 1;
+  g1.N = p.F;
+  g1.K = p.H;
+  g1.B = w->mlp_w1;
+  g1.bias = w->mlp_b1;
+  g1.C = h;
+  g1.n_ntiles = p.F / p.dBN1;
+  const int mt = (int)((p.T + p.dBM - 1) / p.dBM);
+  HIP_TRY(launch_grouped_gemm(p.dtype, EPI_GELU, false, p.dBM, p.dBN1, g1, mt * g1.n_ntiles, s), "dense gemm 1");
+  GemmParams g2{};
+  g2.A = h;
+  g2.M = (int)p.T;
+  g2.nseg = 1;
+  g2.N = p.H;
+  g2.K = p.F;
+  g2.B = w->mlp_w2;
+  g2.bias = w->mlp_b2;
+  g2.C = out;
+  g2.n_ntiles = p.H / p.dBN2;
+  HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, false, p.dBM, p.dBN2, g2, mt * g2.n_ntiles, s), "dense gemm 2");
+  return MOE_OK;
+}
+
+moe_status_t record(hipEvent_t ev, hipStream_t s) {
+  if (ev) HIP_TRY(hipEventRecord(ev, s), "hipEventRecord");
+  return MOE_OK;
+}
+
+#define ST_TRY(expr)                 \
+  do {                               \
+    moe_status_t _s = (expr);        \
+    if (_s != MOE_OK) return _s;     \
+  } while (0)
+
+moe_status_t check_ws(const void* ws, size_t have, size_t need) {
+  if (have < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", have, need);
+  if (need > 0) PTR_TRY(ws, "workspace");
+  return MOE_OK;
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" {
+
+int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double cf) {
+  if (T < 0 || E < 1 || k < 1 || !(cf > 0.0) || !isfinite(cf)) return -1;
+  return capacity_exact(T, E, k, cf);
+}
+
+int64_t moe_max_rows(const moe_layer_desc_t* d) {
+  Plan p;
+  if (validate(d, &p) != MOE_OK) return -1;
+  return p.R_max;
+}
+
+moe_status_t moe_workspace_size(const moe_layer_desc_t* d, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan p;
+  ST_TRY(validate(d, &p));
+  *bytes = p.total;
+  return MOE_OK;
+}
+
+moe_status_t moe_gate(const moe_layer_desc_t* d, const void* x, const void* gate_w, const float* gate_b,
+                      int32_t* topk_idx, float* topk_w, float* probs, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  ST_TRY(validate(d, &p));
+  if (p.T == 0) return MOE_OK;
+  PTR_TRY(x, "x");
+  PTR_TRY(gate_w, "gate_w");
+  PTR_TRY(topk_idx, "topk_idx");
+  PTR_TRY(topk_w, "topk_w");
+  if (gate_b && !aligned16(gate_b)) return fail(MOE_ERR_INVALID_ARGUMENT, "gate_b is not 16-byte aligned");
+  if (probs && !aligned16(probs)) return fail(MOE_ERR_INVALID_ARGUMENT, "probs is not 16-byte aligned");
+  ST_TRY(check_ws(ws, ws_bytes, align_up(p.T * p.E * 4)));
+  float* z = wsp<float>(ws, 0);
+  ST_TRY(run_gate_logits(p, x, gate_w, gate_b, z, stream));
+  HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, topk_idx, topk_w, probs, stream),
+          "softmax/top-k");
+  return MOE_OK;
+}
+
+moe_status_t moe_dispatch(const moe_layer_desc_t* d, const int32_t* topk_idx, const void* x, int32_t* expert_demand,
+                          int32_t* expert_offsets, int32_t* slot_token, int32_t* token_slot, void* x_disp, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  ST_TRY(validate(d, &p));
+  PTR_TRY(expert_demand, "expert_demand");
+  PTR_TRY(expert_offsets, "expert_offsets");
+  // with T == 0 only demand (all zero) and offsets (all zero) are written
+  if (p.T > 0) {
+    PTR_TRY(topk_idx, "topk_idx");
+    PTR_TRY(slot_token, "slot_token");
+    PTR_TRY(token_slot, "token_slot");
+  }
+  if (x_disp && p.T > 0) {
+    PTR_TRY(x, "x");
+    PTR_TRY(x_disp, "x_disp");
+  }
+  // the multi-block path keeps ranks and block histograms at the layer's offsets
+  const size_t need = p.disp_small ? 0 : p.o_blk + (size_t)p.nblk * p.E * 4;
+  ST_TRY(check_ws(ws, ws_bytes, need));
+  ST_TRY(run_dispatch(p, false, nullptr, nullptr, nullptr, (int*)topk_idx, expert_demand, expert_offsets, slot_token,
+                      token_slot, ws, stream));
+  if (x_disp && p.T > 0) HIP_TRY(launch_gather_rows(p.dtype, x, slot_token, (int)p.R_max, p.H, x_disp, stream), "gather");
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_layer_desc_t* d, const void* x_disp, const int32_t* expert_offsets,
+                            const moe_layer_weights_t* w, float* y_disp, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  Plan p;
+  ST_TRY(validate(d, &p));
+  if (p.T == 0 || p.R_max == 0) return MOE_OK;
+  PTR_TRY(x_disp, "x_disp");
+  PTR_TRY(expert_offsets, "expert_offsets");
+  PTR_TRY(y_disp, "y_disp");
+  ST_TRY(check_weights(p, w, true, false));
+  ST_TRY(check_ws(ws, ws_bytes, p.total));
+  ST_TRY(run_experts(p, x_disp, nullptr, expert_offsets, w, y_disp, ws, stream));
+  if (p.exp_decode)
+    HIP_TRY(launch_reduce_partials(wsp<float>(ws, p.o_part), p.P, p.R_max, expert_offsets, p.E_loc, (int)p.R_max,
+                                   p.H, y_disp, stream),
+            "reduce partials");
+  return MOE_OK;
+}
+
+moe_status_t moe_dense_ffn(const moe_layer_desc_t* d, const void* x, const moe_layer_weights_t* w, float* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  ST_TRY(validate(d, &p));
+  if (!p.residual) return fail(MOE_ERR_INVALID_ARGUMENT, "dense MLP needs mlp_type RESIDUAL");
+  if (p.T == 0) return MOE_OK;
+  PTR_TRY(x, "x");
+  PTR_TRY(out, "out");
+  ST_TRY(check_weights(p, w, false, true));
+  ST_TRY(check_ws(ws, ws_bytes, p.total));
+  ST_TRY(run_dense(p, x, w, out, ws, stream));
+  if (p.dense_decode)
+    HIP_TRY(launch_reduce_partials(wsp<float>(ws, p.o_dpart), p.P, p.T, nullptr, 1, (int)p.T, p.H, out, stream),
+            "reduce partials");
+  return MOE_OK;
+}
+
+moe_status_t moe_combine(const moe_layer_desc_t* d, const float* y_disp, const int32_t* token_slot,
+                         const float* topk_w, const float* dense_out, void* y, hipStream_t stream) {
+  Plan p;
+  ST_TRY(validate(d, &p));
+  if (p.T == 0) return MOE_OK;
+  PTR_TRY(token_slot, "token_slot");
+  PTR_TRY(topk_w, "topk_w");
+  PTR_TRY(y, "y");
+  if (p.R_max > 0) PTR_TRY(y_disp, "y_disp");
+  if (dense_out && !aligned16(dense_out)) return fail(MOE_ERR_INVALID_ARGUMENT, "dense_out is not 16-byte aligned");
+  HIP_TRY(launch_combine(p.dtype, y_disp, 1, p.R_max, token_slot, topk_w, p.k, dense_out, 1, y, (int)p.T, p.H,
+                         stream),
+          "combine");
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_weights_t* w, const void* x, void* y,
+                                  void* ws, size_t ws_bytes, hipStream_t stream, const moe_phase_events_t* ev) {
+  Plan p;
+  ST_TRY(validate(d, &p));
+  if (p.T == 0) return MOE_OK;
+  PTR_TRY(x, "x");
+  PTR_TRY(y, "y");
+  if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "weights is NULL");
+  PTR_TRY(w->gate_w, "gate_w");
+  if (w->gate_b && !aligned16(w->gate_b)) return fail(MOE_ERR_INVALID_ARGUMENT, "gate_b is not 16-byte aligned");
+  ST_TRY(check_weights(p, w, true, p.residual));
+  ST_TRY(check_ws(ws, ws_bytes, p.total));
+  const moe_phase_events_t none{};
+  const moe_phase_events_t& e = ev ? *ev : none;
+
+  float* z = wsp<float>(ws, p.o_z);
+  int* idx = wsp<int>(ws, p.o_idx);
+  float* tw = wsp<float>(ws, p.o_w);
+  int* demand = wsp<int>(ws, p.o_demand);
+  int* offsets = wsp<int>(ws, p.o_off);
+  int* slot_token = wsp<int>(ws, p.o_slot_token);
+  int* token_slot = wsp<int>(ws, p.o_token_slot);
+
+  ST_TRY(record(e.gate_begin, stream));
+  ST_TRY(run_gate_logits(p, x, w->gate_w, w->gate_b, z, stream));
+  ST_TRY(record(e.gate_end, stream));
+  ST_TRY(record(e.dispatch_begin, stream));
+  ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot, ws, stream));
+  ST_TRY(record(e.dispatch_end, stream));
+  ST_TRY(record(e.ffn_begin, stream));
+  float* ydisp = p.exp_decode ? nullptr : wsp<float>(ws, p.o_ydisp);
+  if (p.R_max > 0) ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream));
+  float* dense = nullptr;
+  if (p.residual) {
+    dense = p.dense_decode ? wsp<float>(ws, p.o_dpart) : wsp<float>(ws, p.o_dense);
+    ST_TRY(run_dense(p, x, w, dense, ws, stream));
+  }
+  ST_TRY(record(e.ffn_end, stream));
+  ST_TRY(record(e.combine_begin, stream));
+  const float* src = p.exp_decode ? wsp<float>(ws, p.o_part) : ydisp;
+  const int P = p.exp_decode ? p.P : 1;
+  const int Pd = p.dense_decode ? p.P : 1;
+  HIP_TRY(launch_combine(p.dtype, src, P, p.R_max, token_slot, tw, p.k, dense, Pd, y, (int)p.T, p.H, stream),
+          "combine");
+  ST_TRY(record(e.combine_end, stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const moe_layer_weights_t* w, const void* x, void* y,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_layer_forward_ex(d, w, x, y, ws, ws_bytes, stream, nullptr);
+}
+
+const char* moe_status_str(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Wave-level softmax + top-k over one token's gate logits (one wave64 per token).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+#define MOE_MAX_EPL 8    // logits per lane: E <= 512
+
+// Reduce (value, index) pairs to the wave's best: larger value, ties to the
+// lower index. Lanes holding no candidate pass idx = INT_MAX, v = -inf.
+__device__ inline void wave_argmax(float& v, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, MOE_WAVE);
+    int oi = __shfl_xor(idx, o, MOE_WAVE);
+    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+  }
+}
+
+// z: this token's E logits (fp32). Writes idx_out[0..k), w_out[0..k) and, when
+// probs != null, probs[0..E). Softmax is max-subtracted fp32; the choice is made
+// on the logits (ties to the lower expert index), so exp rounding cannot tie.
+// Every lane returns the chosen indices in sel[0..k).
+__device__ inline void wave_softmax_topk(const float* z, int E, int k, bool renorm,
+                                         float* probs, int* idx_out, float* w_out,
+                                         int* sel) {
+  const int lane = lane_id();
+  float v[MOE_MAX_EPL];
+  const int epl = (E + MOE_WAVE - 1) / MOE_WAVE;
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < MOE_MAX_EPL; ++i) {
+    int e = lane + i * MOE_WAVE;
+    v[i] = (i < epl && e < E) ? z[e] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MOE_MAX_EPL; ++i) {
+    int e = lane + i * MOE_WAVE;
+    if (i < epl && e < E) s += expf(v[i] - m);
+  }
+  s = wave_sum(s);
+  const float inv = 1.0f / s;
+  if (probs) {
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_EPL; ++i) {
+      int e = lane + i * MOE_WAVE;
+      if (i < epl && e < E) probs[e] = expf(v[i] - m) * inv;
+    }
+  }
+  float wsel[2] = {0.f, 0.f};
+  sel[0] = sel[1] = -1;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_EPL; ++i) {
+      int e = lane + i * MOE_WAVE;
+      bool ok = (i < epl) && (e < E) && (e != sel[0]);
+      if (ok && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+    if (bi >= E) bi = (j == 0 ? 0 : (sel[0] == 0 ? 1 : 0));  // only if every logit is NaN
+    sel[j] = bi;
+    wsel[j] = expf(bv - m) * inv;
+  }
+  if (renorm) {
+    float t = (k == 2) ? wsel[0] + wsel[1] : wsel[0];
+    wsel[0] /= t;
+    wsel[1] /= t;
+  }
+  if (lane == 0) {
+    for (int j = 0; j < k; ++j) { idx_out[j] = sel[j]; w_out[j] = wsel[j]; }
+  }
+}
+
+}  // namespace moe

@@ -89,7 +89,7 @@ WORKLOADS = {
 # local share), sizes the fp64 oracle finishes in seconds while still spanning
 # several GEMM tiles and ragged segment tails.
 REDUCED = {
-    "prefill_reduced": LayerShape("prefill_reduced", T=1024, H=512, F=1024, E=32, E_loc=32,
+    "prefill_reduced": LayerShape("prefill_reduced", T=1024, H=512, F=1024, E=64, E_loc=64,
                                   k=1, cf=1.25, dtype="f16", zipf_s=1.1),
     "residual_reduced": LayerShape("residual_reduced", T=512, H=256, F=1024, E=16, E_loc=16,
                                    k=1, cf=2.0, dtype="f16", mlp_type="residual"),
