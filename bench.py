@@ -1,0 +1,276 @@
+"""Benchmark: MoE-layer tokens/s on one MI355X, with the dominant kernel's roofline
+fraction and the fp64 oracle timed on the host cores beside it.
+
+A step is one moe_layer_forward (gate, dispatch, expert FFN, combine) over one
+batch of seeded synthetic tokens, inputs and weights resident in HBM. The
+default workload is the 350M+MoE-128 decode step (8 tokens, hidden 1024, FFN
+4096, 128 experts, top-1, capacity factor 1.0, fp16). Steps rotate over 64 token
+batches and over several independent weight sets (layers of a deeper stack),
+so a step does not find the previous step's experts in the 256 MB Infinity
+Cache: every active expert's weights come from HBM, as in a real decode pass.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from mixture_experts_transformer_moe_amd import binding as B  # noqa: E402
+from mixture_experts_transformer_moe_amd import workloads as W  # noqa: E402
+
+METRIC = "MoE-layer tokens/sec at 1 GPU + % of HBM BW (decode) / % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, TFLOP/s
+
+
+# ---------------------------------------------------------------- HIP events via the runtime torch already loaded
+class _Hip:
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.L.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(e)
+
+
+def expert_unit_bytes(shape) -> int:
+    """Algorithmic bytes of one active expert: its W1, b1, W2, b2, read once."""
+    s = 4 if shape.dtype == "f32" else 2
+    return (2 * shape.H * shape.F + shape.F + shape.H) * s
+
+
+def layer_bytes(shape, n_active: int) -> int:
+    """Algorithmic bytes of the whole layer: active experts once, the gate, x and y."""
+    s = 4 if shape.dtype == "f32" else 2
+    b = n_active * expert_unit_bytes(shape) + shape.E * shape.H * s + 2 * shape.T * shape.H * s
+    if shape.zipf_s is not None:
+        b += 4 * shape.E
+    if shape.residual:
+        b += expert_unit_bytes(shape)
+    return b
+
+
+def layer_flops(shape, rows: int) -> int:
+    f = 2 * shape.T * shape.H * shape.E + 4 * shape.H * shape.F * rows
+    if shape.residual:
+        f += 4 * shape.H * shape.F * shape.T
+    return f
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode_350m_moe128", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--layers", type=int, default=None, help="independent weight sets rotated per step")
+    ap.add_argument("--batches", type=int, default=64, help="token batches rotated per step")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the layer on one GPU's expert share "
+              "(no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    shape = W.WORKLOADS[args.workload]
+    n_layers = args.layers if args.layers else (4 if shape.T <= 64 else 1)
+    n_batches = args.batches if shape.T <= 64 else min(args.batches, 2)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs, resident in HBM before any timing
+    weights = [W.make_weights(shape, seed=s, device=dev) for s in range(n_layers)]
+    xs = [W.make_x(shape, seed=1000 + b, device=dev) for b in range(n_batches)]
+    layers = [B.MoELayer(shape, w) for w in weights]
+    ws = layers[0].ws
+    for L in layers[1:]:
+        L.ws = ws
+    y = torch.empty_like(xs[0])
+    torch.cuda.synchronize()
+
+    # routing statistics per (layer, batch), from the gate and dispatch entry points,
+    # read back once outside the timed regions (they size the algorithmic bytes)
+    desc = layers[0].desc
+    R_max = B.moe_max_rows(desc)
+    n_active = np.zeros((n_layers, n_batches), dtype=np.int64)
+    rows = np.zeros((n_layers, n_batches), dtype=np.int64)
+    idx = torch.empty((shape.T, shape.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((shape.T, shape.k), dtype=torch.float32, device=dev)
+    demand = torch.empty(shape.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(shape.E_loc + 1, dtype=torch.int32, device=dev)
+    slot_token = torch.empty(max(R_max, 1), dtype=torch.int32, device=dev)
+    token_slot = torch.empty((shape.T, shape.k), dtype=torch.int32, device=dev)
+    for li in range(n_layers):
+        for bi in range(n_batches):
+            B.moe_gate(desc, xs[bi], weights[li]["gate_w"], weights[li]["gate_b"], idx, tw, None, ws)
+            B.moe_dispatch(desc, idx, xs[bi], demand, offsets, slot_token, token_slot, None, ws)
+            off = offsets.cpu().numpy()
+            n_active[li, bi] = int((np.diff(off) > 0).sum())
+            rows[li, bi] = int(off[-1])
+    del idx, tw, demand, offsets, slot_token, token_slot
+    torch.cuda.synchronize()
+
+    def step(i):
+        layers[i % n_layers].forward(xs[(i // n_layers) % n_batches], y, stream)
+
+    # ---- warmup, then exactly K timed steps
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    tokens_per_s = shape.T * args.steps / (ms_total / 1e3)
+
+    # ---- second pass over the same K steps with per-phase HIP events (same stream)
+    hip = _Hip()
+    names = ["gate", "dispatch", "ffn", "combine"]
+    evs = [[(hip.event(), hip.event()) for _ in names] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        step(i)
+    for i in range(args.steps):
+        pe = B.PhaseEvents(*[e.value for pair in evs[i] for e in pair])
+        layers[i % n_layers].forward(xs[(i // n_layers) % n_batches], y, stream, events=pe)
+    torch.cuda.synchronize()
+    phase_ms = {n: 0.0 for n in names}
+    ffn_bytes = 0
+    ffn_flops = 0
+    for i in range(args.steps):
+        for j, n in enumerate(names):
+            phase_ms[n] += hip.elapsed_ms(evs[i][j][0], evs[i][j][1])
+        li, bi = i % n_layers, (i // n_layers) % n_batches
+        ffn_bytes += int(n_active[li, bi]) * expert_unit_bytes(shape) + (expert_unit_bytes(shape) if shape.residual else 0)
+        ffn_flops += 4 * shape.H * shape.F * int(rows[li, bi]) + (4 * shape.H * shape.F * shape.T if shape.residual else 0)
+    for pairs in evs:
+        for a, b in pairs:
+            hip.destroy(a)
+            hip.destroy(b)
+    ffn_s = phase_ms["ffn"] / 1e3
+    achieved_gbs = ffn_bytes / ffn_s / 1e9
+    achieved_tflops = ffn_flops / ffn_s / 1e12
+    mean_active = float(n_active.mean())
+    mean_rows = float(rows.mean())
+    lay_b = layer_bytes(shape, mean_active)
+    lay_f = layer_flops(shape, mean_rows)
+    hbm_bound = achieved_gbs / HBM_PEAK_GBS >= achieved_tflops / MFMA_F16_PEAK_TFLOPS
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update(kernel="expert FFN phase" if not shape.residual else "expert FFN + dense MLP phase",
+                avg_launch_us=round(phase_ms["ffn"] * 1e3 / args.steps, 2),
+                bytes_per_launch=int(ffn_bytes / args.steps),
+                unit_bytes=expert_unit_bytes(shape), units_per_launch=round(ffn_bytes / args.steps /
+                                                                           expert_unit_bytes(shape), 3))
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic",
+        "config": {"workload": shape.name, "tokens": shape.T, "hidden": shape.H, "ffn": shape.F,
+                   "experts": shape.E, "local_experts": shape.E_loc, "top_k": shape.k,
+                   "capacity_factor": shape.cf, "mlp_type": shape.mlp_type, "weight_sets": n_layers,
+                   "token_batches": n_batches, "parallelism": "one GPU"},
+        "roofline": roof,
+        "layer": {"hbm_frac": round(lay_b / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(lay_f / (ms_per_step / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                  "algorithmic_bytes": int(lay_b), "algorithmic_flops": int(lay_f),
+                  "mean_active_experts": round(mean_active, 3), "mean_rows": round(mean_rows, 2),
+                  "phase_us": {n: round(v * 1e3 / args.steps, 2) for n, v in phase_ms.items()},
+                  "wall_s": round(wall, 3)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, weights[0], xs, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(shape, w, xs, budget_s: float) -> dict:
+    """The fp64 oracle on the same inputs (host copies), over as many token
+    batches as fit in the time budget; tokens/s scaled from that sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    hw = {k: W.to_host_f64_ready(v) for k, v in w.items()}
+    hxs = [W.to_host_f64_ready(x) for x in xs]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.layer_forward(hxs[n % len(hxs)], hw, E=shape.E, k=shape.k, cf=shape.cf, e_lo=shape.e_lo,
+                             E_loc=shape.E_loc, residual=shape.residual, renorm=shape.renorm)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 10000:
+            break
+    return {"value": round(shape.T * n / el, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} layer forwards of {shape.T} tokens (weight set 0, rotating token batches), "
+                      f"{el:.1f} s, numpy float64",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

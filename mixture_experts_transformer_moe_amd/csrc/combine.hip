@@ -45,27 +45,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     acc.x += d.x; acc.y += d.y; acc.z += d.z; acc.w += d.w;
   }
   Tt* dst = y + (long long)t * H + h;
-  dst[0] = DT::from_f(acc.x);
-  dst[1] = DT::from_f(acc.y);
-  dst[2] = DT::from_f(acc.z);
-  dst[3] = DT::from_f(acc.w);
-  }
-}
-
-// out[r] = sum_c part[c][r] for rows r < offsets[nseg] (or r < nrows when offsets is null).
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ part, int P,
-                                                              long long prow, const int* __restrict__ offsets,
-                                                              int nseg, int nrows, int H, float* __restrict__ out) {
-  const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (h >= H) return;
-  const int R = offsets ? offsets[nseg] : nrows;
-  for (int r = blockIdx.y; r < R; r += gridDim.y) {
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < P; ++c) {
-    const float4 u = *reinterpret_cast<const float4*>(part + ((long long)c * prow + r) * H + h);
-    v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
-  }
-  *reinterpret_cast<float4*>(out + (long long)r * H + h) = v;
+  dst[0] = DT::from_f(pin_f32(acc.x));
+  dst[1] = DT::from_f(pin_f32(acc.y));
+  dst[2] = DT::from_f(pin_f32(acc.z));
+  dst[3] = DT::from_f(pin_f32(acc.w));
   }
 }
 
@@ -87,14 +70,6 @@ hipError_t launch_combine(int dtype, const float* ysrc, int P, long long prow, c
       hipLaunchKernelGGL(combine_kernel<DtBF16>, grid, dim3(256), 0, s, ysrc, P, prow, token_slot, w, k, dense,
                          Pd, (__bf16*)y, T, H);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_reduce_partials(const float* part, int P, long long prow, const int* offsets, int nseg,
-                                  int R_max, int H, float* out, hipStream_t s) {
-  if (R_max <= 0) return hipSuccess;
-  dim3 grid((H / 4 + 255) / 256, R_max < 65535 ? R_max : 65535);
-  hipLaunchKernelGGL(reduce_partials_kernel, grid, dim3(256), 0, s, part, P, prow, offsets, nseg, R_max, H, out);
   return hipGetLastError();
 }
 

@@ -60,6 +60,16 @@ __device__ inline float dot16f(const uint4& a, const float* b, float acc) {
   return acc;
 }
 
+// Pin a value to an fp32 register so the compiler cannot fold the following
+// conversion to a narrower type into the operation that produced it (e.g. an
+// fp32 multiply + fp16 conversion into one mixed-precision FMA with a single
+// rounding). Every result is rounded to fp32 first, then to the I/O dtype, the
+// same way on every path.
+__device__ inline float pin_f32(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Exact GeLU u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with the device erff.
 __device__ inline float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
 
@@ -76,6 +86,49 @@ __device__ inline float wave_max(float v) {
 }
 
 __device__ inline int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
+
+// Reduce N per-lane values over the whole wave at once (N a power of two, <= 64).
+// Transpose steps: at offset O each lane pair swaps half of its values, so after
+// log2(N) steps lane l holds one index, l >> (6 - log2 N), summed over the lanes
+// sharing its low bits; plain xor steps over those low bits finish the sum.
+// 63 shuffles for N = 64 instead of 6 N. Every step is unrolled at compile time
+// so the values stay in registers.
+template <int N, int O>
+struct WaveTranspose {
+  __device__ static inline void run(float* v, int lane) {
+    constexpr int h = N / 2;
+    const bool hi = (lane & O) != 0;
+#pragma unroll
+    for (int j = 0; j < h; ++j) {
+      const float send = hi ? v[j] : v[j + h];
+      const float keep = hi ? v[j + h] : v[j];
+      v[j] = keep + __shfl_xor(send, O, 64);
+    }
+    WaveTranspose<h, O / 2>::run(v, lane);
+  }
+};
+template <int O>
+struct WaveTranspose<1, O> {
+  __device__ static inline void run(float*, int) {}
+};
+
+// Returns the wave-wide total of index (lane >> (6 - log2 N)) in every lane.
+template <int N>
+__device__ inline float wave_reduce_multi(float (&v)[N]) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+  const int lane = threadIdx.x & 63;
+  WaveTranspose<N, 32>::run(v, lane);
+  float r = v[0];
+#pragma unroll
+  for (int o = 32 / N; o >= 1; o >>= 1) r += __shfl_xor(r, o, 64);
+  return r;
+}
+
+// All-ones if cond else zero, to mask loaded data without a branch.
+__device__ inline uint4 mask16(const uint4& v, bool cond) {
+  const unsigned m = cond ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -115,18 +168,21 @@ struct GemmParams {
   int n_ntiles;
 };
 
-// Fused small-M expert FFN: each work-group handles one active segment and one
-// BF-wide slice of the FFN width, writing partial outputs part[slice][row][H].
+// Expert FFN for segments of at most MAXM rows: each work-group takes one
+// non-empty segment (or, with seg_off == null, the single segment [0, M)) and
+// a block of weight rows.
 struct DecodeParams {
   const void* x;          // activations [*, H]
-  const int* a_rows;      // row map (slot -> token) or null (dense: rows [0, M))
+  const int* a_rows;      // row map (row -> token) or null (rows index x directly)
   const int* seg_off;     // [nseg + 1] or null
   int nseg;
   int M;                  // rows when seg_off == null
   int H, F;
-  const void* w1; const void* b1; const void* w2; const void* b2;  // [nseg][F][H] ...
-  float* part;            // [F / BF][row_space][H]
-  long long row_space;
+  const void* w1; const void* b1; const void* w2; const void* b2;  // [nseg][F][H], [nseg][F], ...
+  void* h;                // hidden activation [rows][F], I/O dtype (written by up, read by down)
+  void* out;              // down: fp32 [rows][H], or the layer output [T][H] when the combine is folded in
+  const int* slot_token;  // folded combine: token of each row
+  const float* topk_w;    // folded combine: top-1 weight of each token
 };
 
 }  // namespace moe

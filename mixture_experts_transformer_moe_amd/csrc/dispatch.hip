@@ -32,25 +32,27 @@ __device__ inline uint64_t match_lanes(int key, int nbits) {
 
 __device__ inline int key_bits(int E) { return 32 - __clz(E); }   // keys 0..E fit
 
-// Block-level stable ranking of DISP_BLOCK keys in [0, E] (E = "no expert").
+// Block-level stable ranking of NTH keys in [0, E] (E = "no expert").
 // On return: wcnt[w * (E+1) + e] holds the number of keys e in waves < w of this
 // block, *tot (per expert, E entries) the block's count, and the return value
 // is the rank of this thread's key among equal keys of lower threads.
+template <int NTH>
 __device__ inline int block_rank(int key, int E, int* wcnt, int* tot) {
+  constexpr int NW = NTH / MOE_WAVE;
   const int tid = threadIdx.x;
   const int w = tid / MOE_WAVE;
   const int lane = lane_id();
   const int stride = E + 1;
-  for (int i = tid; i < DISP_WAVES * stride; i += DISP_BLOCK) wcnt[i] = 0;
+  for (int i = tid; i < NW * stride; i += NTH) wcnt[i] = 0;
   __syncthreads();
   const uint64_t m = match_lanes(key, key_bits(E));
   const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
   const int rank_w = __popcll(below);
   if (rank_w == 0) wcnt[w * stride + key] = __popcll(m);
   __syncthreads();
-  for (int e = tid; e < E; e += DISP_BLOCK) {
+  for (int e = tid; e < E; e += NTH) {
     int run = 0;
-    for (int ww = 0; ww < DISP_WAVES; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const int c = wcnt[ww * stride + e];
       wcnt[ww * stride + e] = run;
       run += c;
@@ -61,8 +63,10 @@ __device__ inline int block_rank(int key, int E, int* wcnt, int* tot) {
   return (key < E) ? wcnt[w * stride + key] + rank_w : -1;
 }
 
-// Exclusive scan of one int per thread over the whole block (DISP_BLOCK threads).
-__device__ inline int block_excl_scan(int v, int* sh /* DISP_WAVES + 1 ints */, int* total) {
+// Exclusive scan of one int per thread over the whole block (NTH threads).
+template <int NTH>
+__device__ inline int block_excl_scan(int v, int* sh /* NTH / 64 + 1 ints */, int* total) {
+  constexpr int NW = NTH / MOE_WAVE;
   const int lane = lane_id();
   const int w = threadIdx.x / MOE_WAVE;
   int incl = v;
@@ -75,12 +79,12 @@ __device__ inline int block_excl_scan(int v, int* sh /* DISP_WAVES + 1 ints */, 
   __syncthreads();
   if (threadIdx.x == 0) {
     int run = 0;
-    for (int i = 0; i < DISP_WAVES; ++i) { int c = sh[i]; sh[i] = run; run += c; }
-    sh[DISP_WAVES] = run;
+    for (int i = 0; i < NW; ++i) { int c = sh[i]; sh[i] = run; run += c; }
+    sh[NW] = run;
   }
   __syncthreads();
   const int r = sh[w] + incl - v;
-  *total = sh[DISP_WAVES];
+  *total = sh[NW];
   __syncthreads();
   return r;
 }
@@ -90,6 +94,19 @@ __device__ inline int load_key(const int* idx, int a, int T, int k, int E) {
   const int t = a - j * T;
   const int e = idx[(long long)t * k + j];
   return (e >= 0 && e < E) ? e : E;
+}
+
+// Zero the output rows of tokens with no kept local assignment (top-1 layers
+// whose combine is folded into the expert kernel write every other row there).
+template <int ESZ>
+__device__ inline void zero_row(void* y, int t, int H) {
+  uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(y) + (long long)t * H * ESZ);
+  for (int c = 0; c < H * ESZ / 16; ++c) dst[c] = make_uint4(0, 0, 0, 0);
+}
+
+__device__ inline void zero_dropped(void* y_zero, int y_esz, int t, int H) {
+  if (y_esz == 2) zero_row<2>(y_zero, t, H);
+  else zero_row<4>(y_zero, t, H);
 }
 
 // -------------------------------------------------------------------- multi-block path
@@ -102,7 +119,7 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_count_kernel(const int* _
   const int kT = T * k;
   const int a = blockIdx.x * DISP_BLOCK + threadIdx.x;
   const int key = (a < kT) ? load_key(idx, a, T, k, E) : E;
-  const int r = block_rank(key, E, wcnt, tot);
+  const int r = block_rank<DISP_BLOCK>(key, E, wcnt, tot);
   for (int e = threadIdx.x; e < E; e += DISP_BLOCK) blk_hist[(long long)blockIdx.x * E + e] = tot[e];
   if (a < kT) rank[a] = r;
 }
@@ -129,7 +146,7 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scan_kernel(int* __restri
   __syncthreads();
   const int kept = (tid < E_loc) ? min(sdem[e_lo + tid], C) : 0;
   int total;
-  const int off = block_excl_scan(kept, ssc, &total);
+  const int off = block_excl_scan<DISP_BLOCK>(kept, ssc, &total);
   if (tid < E_loc) offsets[tid] = off;
   if (tid == 0) offsets[E_loc] = total;
 }
@@ -137,7 +154,7 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scan_kernel(int* __restri
 __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
     const int* __restrict__ idx, const int* __restrict__ rank, const int* __restrict__ base, int T, int k,
     int E, int e_lo, int E_loc, int C, const int* __restrict__ offsets, int R_max,
-    int* __restrict__ slot_token, int* __restrict__ token_slot) {
+    int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H) {
   const int kT = T * k;
   const int a = blockIdx.x * DISP_BLOCK + threadIdx.x;
   if (a < kT) {
@@ -153,6 +170,7 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
       }
     }
     token_slot[(long long)t * k + j] = slot;
+    if (y_zero && slot < 0) zero_dropped(y_zero, y_esz, t, H);
   }
   const int R = offsets[E_loc];
   for (int s = R + blockIdx.x * DISP_BLOCK + threadIdx.x; s < R_max; s += gridDim.x * DISP_BLOCK)
@@ -160,23 +178,24 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
 }
 
 // -------------------------------------------------------------------- one-block path
-// Whole dispatch for k*T <= DISP_BLOCK in one launch; with FUSE_TOPK it first
-// runs the softmax / top-k of every token from the logits z (one wave per token).
-template <bool FUSE_TOPK>
-__global__ __launch_bounds__(DISP_BLOCK) void dispatch_small_kernel(
-    const float* z, int renorm, float* probs, float* __restrict__ topk_w, int* idx, int T, int k, int E,
-    int e_lo, int E_loc, int C, int R_max, int* __restrict__ demand, int* __restrict__ offsets,
-    int* __restrict__ slot_token, int* __restrict__ token_slot) {
-  extern __shared__ int sh[];
-  int* wcnt = sh;                                   // DISP_WAVES * (E + 1)
-  int* tot = wcnt + DISP_WAVES * (E + 1);           // E
-  int* sidx = tot + E;                              // DISP_BLOCK
-  int* ssc = sidx + DISP_BLOCK;                     // DISP_WAVES + 1
+// Whole dispatch for k*T <= NTH in one block of NTH threads. MODE 0: the routing
+// comes from idx; MODE 1: softmax / top-k of every token first, from logits z
+// (one wave per token). sh must hold small_lds_ints<NTH>(E) ints.
+template <int MODE, int NTH>
+__device__ inline void dispatch_small_body(int* sh, const float* z, int renorm, float* probs, float* topk_w, int* idx,
+                                           int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
+                                           int* demand, int* offsets, int* slot_token, int* token_slot,
+                                           void* y_zero, int y_esz, int H) {
+  constexpr int NW = NTH / MOE_WAVE;
+  int* wcnt = sh;                                   // NW * (E + 1)
+  int* tot = wcnt + NW * (E + 1);                   // E
+  int* sidx = tot + E;                              // NTH
+  int* ssc = sidx + NTH;                            // NW + 1
   const int tid = threadIdx.x;
   const int kT = T * k;
-  if (FUSE_TOPK) {
+  if (MODE == 1) {
     const int w = tid / MOE_WAVE;
-    for (int t = w; t < T; t += DISP_WAVES) {
+    for (int t = w; t < T; t += NW) {
       int sel[2];
       wave_softmax_topk(z + (long long)t * E, E, k, renorm != 0, probs ? probs + (long long)t * E : nullptr,
                         idx + (long long)t * k, topk_w + (long long)t * k, sel);
@@ -187,18 +206,18 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_small_kernel(
   }
   int key = E;
   if (tid < kT) {
-    if (FUSE_TOPK) {
+    if (MODE == 1) {
       const int e = sidx[tid];
       key = (e >= 0 && e < E) ? e : E;
     } else {
       key = load_key(idx, tid, T, k, E);
     }
   }
-  const int r = block_rank(key, E, wcnt, tot);
-  for (int e = tid; e < E; e += DISP_BLOCK) demand[e] = tot[e];
+  const int r = block_rank<NTH>(key, E, wcnt, tot);
+  for (int e = tid; e < E; e += NTH) demand[e] = tot[e];
   const int kept = (tid < E_loc) ? min(tot[e_lo + tid], C) : 0;
   int total;
-  const int off = block_excl_scan(kept, ssc, &total);
+  const int off = block_excl_scan<NTH>(kept, ssc, &total);
   if (tid < E_loc) sidx[tid] = off;   // reuse: segment offsets (the keys are already in registers)
   if (tid < E_loc) offsets[tid] = off;
   if (tid == 0) offsets[E_loc] = total;
@@ -212,8 +231,19 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_small_kernel(
       slot_token[slot] = t;
     }
     token_slot[(long long)t * k + j] = slot;
+    if (y_zero && slot < 0) zero_dropped(y_zero, y_esz, t, H);
   }
-  for (int s = total + tid; s < R_max; s += DISP_BLOCK) slot_token[s] = -1;
+  for (int s = total + tid; s < R_max; s += NTH) slot_token[s] = -1;
+}
+
+template <int MODE, int NTH>
+__global__ __launch_bounds__(NTH) void dispatch_small_kernel(
+    const float* z, int renorm, float* probs, float* __restrict__ topk_w, int* idx, int T, int k, int E,
+    int e_lo, int E_loc, int C, int R_max, int* __restrict__ demand, int* __restrict__ offsets,
+    int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H) {
+  extern __shared__ int sh[];
+  dispatch_small_body<MODE, NTH>(sh, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets,
+                                 slot_token, token_slot, y_zero, y_esz, H);
 }
 
 // Gather x rows into the dispatched order (zero rows past the last one).
@@ -234,23 +264,36 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const typename DT::T* 
 }
 
 // -------------------------------------------------------------------- launchers
-size_t dispatch_small_lds(int E) {
-  return sizeof(int) * ((size_t)DISP_WAVES * (E + 1) + E + DISP_BLOCK + DISP_WAVES + 1);
+template <int NTH>
+static size_t small_lds(int E) {
+  return sizeof(int) * ((size_t)(NTH / MOE_WAVE) * (E + 1) + E + NTH + NTH / MOE_WAVE + 1);
+}
+size_t dispatch_small_lds(int E) { return small_lds<DISP_BLOCK>(E); }
+
+template <int NTH>
+static void launch_small_t(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w, int* idx, int T,
+                           int k, int E, int e_lo, int E_loc, int C, int R_max, int* demand, int* offsets,
+                           int* slot_token, int* token_slot, void* y_zero, int y_esz, int H, hipStream_t s) {
+  const size_t lds = small_lds<NTH>(E);
+  if (fuse_topk)
+    hipLaunchKernelGGL((dispatch_small_kernel<1, NTH>), dim3(1), dim3(NTH), lds, s, z, renorm, probs, topk_w, idx, T,
+                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H);
+  else
+    hipLaunchKernelGGL((dispatch_small_kernel<0, NTH>), dim3(1), dim3(NTH), lds, s, z, renorm, probs, topk_w, idx, T,
+                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H);
 }
 
+// One block of 256 threads when the assignments and local experts fit, else 1024.
 hipError_t launch_dispatch_small(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w,
                                  int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
-                                 int* demand, int* offsets, int* slot_token, int* token_slot,
-                                 hipStream_t s) {
-  const size_t lds = dispatch_small_lds(E);
-  if (fuse_topk)
-    hipLaunchKernelGGL(dispatch_small_kernel<true>, dim3(1), dim3(DISP_BLOCK), lds, s, z, renorm, probs,
-                       topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token,
-                       token_slot);
+                                 int* demand, int* offsets, int* slot_token, int* token_slot, void* y_zero,
+                                 int y_esz, int H, hipStream_t s) {
+  if (T * k <= 256 && E_loc <= 256)
+    launch_small_t<256>(fuse_topk, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets,
+                        slot_token, token_slot, y_zero, y_esz, H, s);
   else
-    hipLaunchKernelGGL(dispatch_small_kernel<false>, dim3(1), dim3(DISP_BLOCK), lds, s, z, renorm, probs,
-                       topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token,
-                       token_slot);
+    launch_small_t<DISP_BLOCK>(fuse_topk, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand,
+                               offsets, slot_token, token_slot, y_zero, y_esz, H, s);
   return hipGetLastError();
 }
 
@@ -259,7 +302,7 @@ int dispatch_block_size() { return DISP_BLOCK; }
 
 hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* rank, int* blk_hist, int* demand, int* offsets, int* slot_token,
-                                 int* token_slot, hipStream_t s) {
+                                 int* token_slot, void* y_zero, int y_esz, int H, hipStream_t s) {
   const int nblk = dispatch_num_blocks((long long)T * k);
   const size_t lds = sizeof(int) * ((size_t)DISP_WAVES * (E + 1) + E);
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(DISP_BLOCK), lds, s, idx, T, k, E, rank,
@@ -271,7 +314,7 @@ hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, 
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(DISP_BLOCK), 0, s, idx, rank, blk_hist, T, k,
-                     E, e_lo, E_loc, C, offsets, R_max, slot_token, token_slot);
+                     E, e_lo, E_loc, C, offsets, R_max, slot_token, token_slot, y_zero, y_esz, H);
   return hipGetLastError();
 }
 

@@ -120,20 +120,22 @@ __global__ __launch_bounds__(GEMM_THREADS) void grouped_gemm_kernel(GemmParams p
   const int wave_n = wave % WN;
   const int wave_m = wave / WN;
 
-  // ---- per-thread global source rows
+  // ---- per-thread global source rows. With BM = 16 only half the threads own an
+  // activation chunk; the others load a valid duplicate and skip the LDS store,
+  // so every load is unconditional and all of them stay in flight together.
   const char* a_src[ACH];
   int a_dst[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
-    const int c = tid + i * GEMM_THREADS;
+    const int c = min(tid + i * GEMM_THREADS, BM * 8 - 1);
     const int row = c >> 3, col = c & 7;
     int r = m0 + row;
     if (r >= r1) r = r1 - 1;
     const long long arow = p.a_rows ? (long long)p.a_rows[r] : (long long)r;
-    a_src[i] = (c < BM * 8) ? reinterpret_cast<const char*>(p.A) + (arow * p.K) * (long long)sizeof(T) + col * 16
-                            : nullptr;
+    a_src[i] = reinterpret_cast<const char*>(p.A) + (arow * p.K) * (long long)sizeof(T) + col * 16;
     a_dst[i] = BN * LDS_ROW + row * LDS_ROW + col * 16;
   }
+  const bool a_own = (BM * 8 >= GEMM_THREADS) || (tid < BM * 8);
   const char* b_src[BCH];
   int b_dst[BCH];
   const char* bbase = reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
@@ -152,35 +154,36 @@ __global__ __launch_bounds__(GEMM_THREADS) void grouped_gemm_kernel(GemmParams p
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[ACH], rb[BCH];
+  u32x4_t ra[ACH], rb[BCH];
   const int nk = (int)(((long long)p.K * sizeof(T)) / 128);
-
-  auto gload = [&](int ks) {
-    const long long off = (long long)ks * 128;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      if (a_src[i]) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + off);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + off);
-  };
-  auto lstore = [&](int buf) {
-    char* base = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      if (a_src[i]) *reinterpret_cast<uint4*>(base + a_dst[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) *reinterpret_cast<uint4*>(base + b_dst[i]) = rb[i];
-  };
-
   const int frag_row = lane & 15;
   const int frag_k = (lane >> 4) * 16;   // byte offset within a 64-byte k-block
 
-  gload(0);
-  lstore(0);
+// global -> registers for stage KS (all loads of the stage in flight together)
+#define GEMM_GLOAD(KS)                                                                   \
+  {                                                                                      \
+    const long long off_ = (long long)(KS) * 128;                                        \
+    _Pragma("unroll") for (int i = 0; i < ACH; ++i) ra[i] =                              \
+        *reinterpret_cast<const u32x4_t*>(a_src[i] + off_);                              \
+    _Pragma("unroll") for (int i = 0; i < BCH; ++i) rb[i] =                              \
+        *reinterpret_cast<const u32x4_t*>(b_src[i] + off_);                              \
+  }
+// registers -> LDS buffer BUF
+#define GEMM_LSTORE(BUF)                                                                 \
+  {                                                                                      \
+    char* base_ = smem + (BUF) * STAGE;                                                  \
+    _Pragma("unroll") for (int i = 0; i < ACH; ++i) if (a_own)                           \
+        *reinterpret_cast<u32x4_t*>(base_ + a_dst[i]) = ra[i];                           \
+    _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                      \
+        *reinterpret_cast<u32x4_t*>(base_ + b_dst[i]) = rb[i];                           \
+  }
+
+  GEMM_GLOAD(0);
+  GEMM_LSTORE(0);
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
     const int buf = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
+    if (ks + 1 < nk) GEMM_GLOAD(ks + 1);
     const char* sb = smem + buf * STAGE;
     const char* sa = sb + BN * LDS_ROW;
 #pragma unroll
@@ -199,9 +202,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void grouped_gemm_kernel(GemmParams p
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = Mfma<DT>::op(fa[i], fb[j], acc[i][j]);
     }
-    if (ks + 1 < nk) lstore(buf ^ 1);
+    if (ks + 1 < nk) GEMM_LSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef GEMM_GLOAD
+#undef GEMM_LSTORE
 
   // ---- epilogue: lane holds D[n = 4*(lane/16) + q][m = lane % 16], q = 0..3
   const BiasT* bias = p.bias ? reinterpret_cast<const BiasT*>(p.bias) + (long long)seg * p.bias_stride : nullptr;
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void grouped_gemm_kernel(GemmParams p
       if constexpr (EPI == EPI_GELU) {
         T o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = DT::from_f(gelu_erf(v[q]));
+        for (int q = 0; q < 4; ++q) o[q] = DT::from_f(pin_f32(gelu_erf(v[q])));
         T* dst = reinterpret_cast<T*>(p.C) + (long long)r * p.N + n;
         if constexpr (sizeof(T) == 2) {
           *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o);

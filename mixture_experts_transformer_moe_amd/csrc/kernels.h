@@ -18,13 +18,14 @@ hipError_t launch_softmax_topk(const float* z, int T, int E, int k, int renorm, 
 size_t dispatch_small_lds(int E);
 int dispatch_num_blocks(long long kT);
 int dispatch_block_size();
+// y_zero (nullable): output rows of tokens with no kept assignment are zeroed there.
 hipError_t launch_dispatch_small(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w,
                                  int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
-                                 int* demand, int* offsets, int* slot_token, int* token_slot,
-                                 hipStream_t s);
+                                 int* demand, int* offsets, int* slot_token, int* token_slot, void* y_zero,
+                                 int y_esz, int H, hipStream_t s);
 hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* rank, int* blk_hist, int* demand, int* offsets, int* slot_token,
-                                 int* token_slot, hipStream_t s);
+                                 int* token_slot, void* y_zero, int y_esz, int H, hipStream_t s);
 hipError_t launch_gather_rows(int dtype, const void* x, const int* slot_token, int R_max, int H, void* xd,
                               hipStream_t s);
 
@@ -39,15 +40,14 @@ hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN
                                int grid, hipStream_t s);
 
 // decode_ffn.hip
-constexpr int DECODE_BF = 64;
-size_t decode_ffn_lds(int dtype, int maxm, int H);
-hipError_t launch_decode_ffn(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s);
+bool decode_supported(int dtype, int H, int F);
+hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s);
+hipError_t launch_decode_down(int dtype, int maxm, const DecodeParams& p, int grid_segs, bool fuse_combine,
+                              hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(int dtype, const float* ysrc, int P, long long prow, const int* token_slot,
                           const float* w, int k, const float* dense, int Pd, void* y, int T, int H,
                           hipStream_t s);
-hipError_t launch_reduce_partials(const float* part, int P, long long prow, const int* offsets, int nseg,
-                                  int R_max, int H, float* out, hipStream_t s);
 
 }  // namespace moe

@@ -39,7 +39,6 @@ moe_status_t hip_fail(hipError_t e, const char* where) {
 
 constexpr int kMaxExperts = 512;
 constexpr size_t kAlign = 256;
-constexpr size_t kDecodeLdsMax = 48 * 1024;   // x rows staged in LDS by the decode kernel
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -93,17 +92,17 @@ struct Plan {
   bool disp_small;
   int nblk;
   // experts
-  bool exp_decode;
+  bool exp_decode;   // streaming kernels for segments of <= 8 rows, else grouped MFMA GEMM
+  bool fold_combine; // top-1 standard layer on the decode path: the expert kernel writes y
   int exp_maxm;
   int BM, BN1, BN2, mt_bound;
-  int P;  // decode slices
   // dense MLP
   bool dense_decode;
   int dense_maxm, dBM, dBN1, dBN2;
   // workspace offsets (bytes)
   size_t o_z, o_idx, o_w, o_rank, o_blk, o_demand, o_off, o_slot_token, o_token_slot;
-  size_t o_part, o_h, o_ydisp, o_list1, o_list2, o_count;
-  size_t o_dpart, o_dh, o_dense;
+  size_t o_h, o_ydisp, o_list1, o_list2, o_count;
+  size_t o_dh, o_dense;
   size_t total;
 };
 
@@ -152,19 +151,18 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   if ((int64_t)p.R_max * std::max(p.H, p.F) > ((int64_t)1 << 40))
     return fail(MOE_ERR_UNSUPPORTED, "dispatched buffers too large");
 
-  // gate: matrix cores when the batch fills tiles, else one wave per expert
-  p.gate_mfma = p.T >= 64 && (p.E % 64) == 0;
-  p.gate_BM = 64;
-  p.gate_BN = (p.E % 128 == 0) ? 128 : 64;
   // dispatch: one block when every assignment fits in it
   p.disp_small = kT <= dispatch_block_size();
   p.nblk = dispatch_num_blocks(kT);
-  // experts: fused streaming kernel for tiny segments, grouped MFMA GEMM otherwise
+  // gate: matrix cores when the batch fills tiles; else 4x8 wave blocks on the ALUs
+  p.gate_mfma = p.T >= 64 && (p.E % 64) == 0;
+  p.gate_BM = 64;
+  p.gate_BN = (p.E % 128 == 0) ? 128 : 64;
+  // experts: streaming kernels for tiny segments, grouped MFMA GEMM otherwise
   const int64_t seg_rows = std::min<int64_t>(p.C, kT);
   p.exp_maxm = pow2_at_least(std::max<int64_t>(seg_rows, 1));
-  p.exp_decode = p.dtype != DT_F32 && seg_rows <= 8 && p.H % 512 == 0 &&
-                 decode_ffn_lds(p.dtype, p.exp_maxm, p.H) <= kDecodeLdsMax;
-  p.P = p.F / DECODE_BF;
+  p.exp_decode = seg_rows <= 8 && decode_supported(p.dtype, p.H, p.F);
+  p.fold_combine = p.exp_decode && p.k == 1 && !p.residual;
   p.BM = gemm_bm_for_rows(seg_rows);
   p.BN1 = (p.F % 128 == 0) ? 128 : 64;
   p.BN2 = (p.H % 128 == 0) ? 128 : 64;
@@ -176,8 +174,7 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
     if (p.F / p.BN1 >= 65536 || p.H / p.BN2 >= 65536) return fail(MOE_ERR_UNSUPPORTED, "too many column tiles");
   }
   p.dense_maxm = pow2_at_least(std::max<int64_t>(p.T, 1));
-  p.dense_decode = p.dtype != DT_F32 && p.T <= 8 && p.H % 512 == 0 &&
-                   decode_ffn_lds(p.dtype, p.dense_maxm, p.H) <= kDecodeLdsMax;
+  p.dense_decode = p.T <= 8 && decode_supported(p.dtype, p.H, p.F);
   p.dBM = gemm_bm_for_rows(p.T);
   p.dBN1 = p.BN1;
   p.dBN2 = p.BN2;
@@ -199,22 +196,16 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   p.o_off = take((size_t)(p.E_loc + 1) * 4);
   p.o_slot_token = take(R * 4);
   p.o_token_slot = take(T * p.k * 4);
-  if (p.exp_decode) {
-    p.o_part = take((size_t)p.P * R * H * 4);
-  } else {
-    p.o_h = take(R * F * p.esz);
-    p.o_ydisp = take(R * H * 4);
+  p.o_h = take(R * F * p.esz);
+  p.o_ydisp = take(R * H * 4);
+  if (!p.exp_decode) {
     p.o_list1 = take((size_t)p.mt_bound * (F / p.BN1) * sizeof(int2));
     p.o_list2 = take((size_t)p.mt_bound * (H / p.BN2) * sizeof(int2));
     p.o_count = take(4);
   }
   if (p.residual) {
-    if (p.dense_decode) {
-      p.o_dpart = take((size_t)p.P * T * H * 4);
-    } else {
-      p.o_dh = take(T * F * p.esz);
-      p.o_dense = take(T * H * 4);
-    }
+    p.o_dh = take(T * F * p.esz);
+    p.o_dense = take(T * H * 4);
   }
   p.total = o;
   return MOE_OK;
@@ -278,17 +269,20 @@ moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, c
 }
 
 moe_status_t run_dispatch(const Plan& p, bool fuse_topk, const float* z, float* probs, float* topk_w, int* idx,
-                          int* demand, int* offsets, int* slot_token, int* token_slot, void* ws, hipStream_t s) {
+                          int* demand, int* offsets, int* slot_token, int* token_slot, void* y_zero, void* ws,
+                          hipStream_t s) {
   const int C = (int)std::min<int64_t>(p.C, INT32_MAX);
   if (p.disp_small) {
     HIP_TRY(launch_dispatch_small(fuse_topk, z, p.renorm ? 1 : 0, probs, topk_w, idx, (int)p.T, p.k, p.E, p.e_lo,
-                                  p.E_loc, C, (int)p.R_max, demand, offsets, slot_token, token_slot, s),
+                                  p.E_loc, C, (int)p.R_max, demand, offsets, slot_token, token_slot, y_zero,
+                                  (int)p.esz, p.H, s),
             "dispatch (one block)");
   } else {
     if (fuse_topk)
       HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, idx, topk_w, probs, s), "softmax/top-k");
     HIP_TRY(launch_dispatch_multi(idx, (int)p.T, p.k, p.E, p.e_lo, p.E_loc, C, (int)p.R_max, wsp<int>(ws, p.o_rank),
-                                  wsp<int>(ws, p.o_blk), demand, offsets, slot_token, token_slot, s),
+                                  wsp<int>(ws, p.o_blk), demand, offsets, slot_token, token_slot, y_zero,
+                                  (int)p.esz, p.H, s),
             "dispatch");
   }
   return MOE_OK;
@@ -297,7 +291,8 @@ moe_status_t run_dispatch(const Plan& p, bool fuse_topk, const float* z, float* 
 // Expert FFN. x rows come from x via slot_token (a_rows != null) or from
 // x_disp directly. Decode path leaves partials in ws; GEMM path writes ydisp.
 moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const int* offsets,
-                         const moe_layer_weights_t* w, float* ydisp, void* ws, hipStream_t s) {
+                         const moe_layer_weights_t* w, float* ydisp, void* ws, hipStream_t s,
+                         void* y_fold = nullptr, const int* slot_token = nullptr, const float* topk_w = nullptr) {
   if (p.exp_decode) {
     DecodeParams d{};
     d.x = x;
@@ -310,10 +305,13 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
     d.b1 = w->b1;
     d.w2 = w->w2;
     d.b2 = w->b2;
-    d.part = wsp<float>(ws, p.o_part);
-    d.row_space = p.R_max;
+    d.h = wsp<void>(ws, p.o_h);
+    d.out = y_fold ? y_fold : (void*)ydisp;
+    d.slot_token = slot_token;
+    d.topk_w = topk_w;
     const int gsegs = (int)std::min<int64_t>(p.E_loc, p.R_max);
-    HIP_TRY(launch_decode_ffn(p.dtype, p.exp_maxm, d, gsegs, s), "expert ffn (decode)");
+    HIP_TRY(launch_decode_up(p.dtype, p.exp_maxm, d, gsegs, s), "expert ffn up (decode)");
+    HIP_TRY(launch_decode_down(p.dtype, p.exp_maxm, d, gsegs, y_fold != nullptr, s), "expert ffn down (decode)");
     return MOE_OK;
   }
   int2* l1 = wsp<int2>(ws, p.o_list1);
@@ -356,7 +354,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   return MOE_OK;
 }
 
-// Dense MLP (residual mode). Decode path leaves partials at o_dpart; GEMM path writes out.
+// Dense MLP (residual mode) over all T rows into out [T, H] fp32.
 moe_status_t run_dense(const Plan& p, const void* x, const moe_layer_weights_t* w, float* out, void* ws,
                        hipStream_t s) {
   if (p.dense_decode) {
@@ -370,9 +368,10 @@ moe_status_t run_dense(const Plan& p, const void* x, const moe_layer_weights_t* 
     d.b1 = w->mlp_b1;
     d.w2 = w->mlp_w2;
     d.b2 = w->mlp_b2;
-    d.part = wsp<float>(ws, p.o_dpart);
-    d.row_space = p.T;
-    HIP_TRY(launch_decode_ffn(p.dtype, p.dense_maxm, d, 1, s), "dense mlp (decode)");
+    d.h = wsp<void>(ws, p.o_dh);
+    d.out = out;
+    HIP_TRY(launch_decode_up(p.dtype, p.dense_maxm, d, 1, s), "dense mlp up (decode)");
+    HIP_TRY(launch_decode_down(p.dtype, p.dense_maxm, d, 1, false, s), "dense mlp down (decode)");
     return MOE_OK;
   }
   void* h = wsp<void>(ws, p.o_dh);
@@ -484,7 +483,7 @@ moe_status_t moe_dispatch(const moe_layer_desc_t* d, const int32_t* topk_idx, co
   const size_t need = p.disp_small ? 0 : p.o_blk + (size_t)p.nblk * p.E * 4;
   ST_TRY(check_ws(ws, ws_bytes, need));
   ST_TRY(run_dispatch(p, false, nullptr, nullptr, nullptr, (int*)topk_idx, expert_demand, expert_offsets, slot_token,
-                      token_slot, ws, stream));
+                      token_slot, nullptr, ws, stream));
   if (x_disp && p.T > 0) HIP_TRY(launch_gather_rows(p.dtype, x, slot_token, (int)p.R_max, p.H, x_disp, stream), "gather");
   return MOE_OK;
 }
@@ -501,10 +500,6 @@ moe_status_t moe_expert_ffn(const moe_layer_desc_t* d, const void* x_disp, const
   ST_TRY(check_weights(p, w, true, false));
   ST_TRY(check_ws(ws, ws_bytes, p.total));
   ST_TRY(run_experts(p, x_disp, nullptr, expert_offsets, w, y_disp, ws, stream));
-  if (p.exp_decode)
-    HIP_TRY(launch_reduce_partials(wsp<float>(ws, p.o_part), p.P, p.R_max, expert_offsets, p.E_loc, (int)p.R_max,
-                                   p.H, y_disp, stream),
-            "reduce partials");
   return MOE_OK;
 }
 
@@ -519,9 +514,6 @@ moe_status_t moe_dense_ffn(const moe_layer_desc_t* d, const void* x, const moe_l
   ST_TRY(check_weights(p, w, false, true));
   ST_TRY(check_ws(ws, ws_bytes, p.total));
   ST_TRY(run_dense(p, x, w, out, ws, stream));
-  if (p.dense_decode)
-    HIP_TRY(launch_reduce_partials(wsp<float>(ws, p.o_dpart), p.P, p.T, nullptr, 1, (int)p.T, p.H, out, stream),
-            "reduce partials");
   return MOE_OK;
 }
 
@@ -564,27 +556,26 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   int* slot_token = wsp<int>(ws, p.o_slot_token);
   int* token_slot = wsp<int>(ws, p.o_token_slot);
 
+  void* y_fold = p.fold_combine ? y : nullptr;
   ST_TRY(record(e.gate_begin, stream));
   ST_TRY(run_gate_logits(p, x, w->gate_w, w->gate_b, z, stream));
   ST_TRY(record(e.gate_end, stream));
   ST_TRY(record(e.dispatch_begin, stream));
-  ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot, ws, stream));
+  ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot, y_fold, ws, stream));
   ST_TRY(record(e.dispatch_end, stream));
   ST_TRY(record(e.ffn_begin, stream));
-  float* ydisp = p.exp_decode ? nullptr : wsp<float>(ws, p.o_ydisp);
-  if (p.R_max > 0) ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream));
+  float* ydisp = wsp<float>(ws, p.o_ydisp);
+  if (p.R_max > 0) ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream, y_fold, slot_token, tw));
   float* dense = nullptr;
   if (p.residual) {
-    dense = p.dense_decode ? wsp<float>(ws, p.o_dpart) : wsp<float>(ws, p.o_dense);
+    dense = wsp<float>(ws, p.o_dense);
     ST_TRY(run_dense(p, x, w, dense, ws, stream));
   }
   ST_TRY(record(e.ffn_end, stream));
   ST_TRY(record(e.combine_begin, stream));
-  const float* src = p.exp_decode ? wsp<float>(ws, p.o_part) : ydisp;
-  const int P = p.exp_decode ? p.P : 1;
-  const int Pd = p.dense_decode ? p.P : 1;
-  HIP_TRY(launch_combine(p.dtype, src, P, p.R_max, token_slot, tw, p.k, dense, Pd, y, (int)p.T, p.H, stream),
-          "combine");
+  if (!p.fold_combine)
+    HIP_TRY(launch_combine(p.dtype, ydisp, 1, p.R_max, token_slot, tw, p.k, dense, 1, y, (int)p.T, p.H, stream),
+            "combine");
   ST_TRY(record(e.combine_end, stream));
   return MOE_OK;
 }

@@ -33,6 +33,10 @@ CASES = {
     "k2_e2": W.LayerShape("k2_e2", T=200, H=128, F=256, E=2, E_loc=2, k=2, cf=0.75, dtype="f16"),
     "e1_dense": W.LayerShape("e1", T=100, H=64, F=192, E=1, E_loc=1, k=1, cf=1.0, dtype="f16"),
     "gemm_mid_rows": W.LayerShape("mid", T=600, H=256, F=512, E=8, E_loc=8, k=2, cf=1.0, dtype="f16"),
+    "decode_f32_h512": W.LayerShape("dec32", T=8, H=512, F=512, E=32, E_loc=32, k=1, cf=1.0, dtype="f32"),
+    "decode_f32_h256_k2": W.LayerShape("dec32b", T=5, H=256, F=256, E=16, E_loc=16, k=2, cf=2.0, dtype="f32"),
+    "decode_k2_share": W.LayerShape("deck2", T=8, H=1024, F=2048, E=64, E_loc=16, e_lo=16, k=2, cf=1.0,
+                                    dtype="f16"),
 }
 
 
