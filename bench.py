@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--batches", type=int, default=64, help="token batches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, copy a buffer of this size 3 times (reference kernel for HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -162,32 +164,41 @@ def main():
     ms_per_step = ms_total / args.steps
     tokens_per_s = shape.T * args.steps / (ms_total / 1e3)
 
-    # ---- second pass over the same K steps with per-phase HIP events (same stream)
+    # ---- second pass over the same K steps with per-phase HIP events (same stream):
+    # gate, dispatch, the two expert kernels (W1 kernel "up", W2 kernel "down"), combine
     hip = _Hip()
-    names = ["gate", "dispatch", "ffn", "combine"]
-    evs = [[(hip.event(), hip.event()) for _ in names] for _ in range(args.steps)]
+    names = ["gate", "dispatch", "up", "down", "combine"]
+    pairs = [("gate_begin", "gate_end"), ("dispatch_begin", "dispatch_end"), ("ffn_begin", "ffn_split"),
+             ("ffn_split", "ffn_end"), ("combine_begin", "combine_end")]
+    fields = [f for f, _ in B.PhaseEvents._fields_]
+    evs = [{f: hip.event() for f in fields} for _ in range(args.steps)]
     for i in range(args.warmup):
         step(i)
     for i in range(args.steps):
-        pe = B.PhaseEvents(*[e.value for pair in evs[i] for e in pair])
+        pe = B.PhaseEvents(**{f: e.value for f, e in evs[i].items()})
         layers[i % n_layers].forward(xs[(i // n_layers) % n_batches], y, stream, events=pe)
     torch.cuda.synchronize()
     phase_ms = {n: 0.0 for n in names}
-    ffn_bytes = 0
-    ffn_flops = 0
+    s_w = 4 if shape.dtype == "f32" else 2
+    HF = shape.H * shape.F
+    win_bytes = {"up": 0, "down": 0}
+    win_flops = {"up": 0, "down": 0}
     for i in range(args.steps):
-        for j, n in enumerate(names):
-            phase_ms[n] += hip.elapsed_ms(evs[i][j][0], evs[i][j][1])
+        for n, (a, b) in zip(names, pairs):
+            phase_ms[n] += hip.elapsed_ms(evs[i][a], evs[i][b])
         li, bi = i % n_layers, (i // n_layers) % n_batches
-        ffn_bytes += int(n_active[li, bi]) * expert_unit_bytes(shape) + (expert_unit_bytes(shape) if shape.residual else 0)
-        ffn_flops += 4 * shape.H * shape.F * int(rows[li, bi]) + (4 * shape.H * shape.F * shape.T if shape.residual else 0)
-    for pairs in evs:
-        for a, b in pairs:
-            hip.destroy(a)
-            hip.destroy(b)
-    ffn_s = phase_ms["ffn"] / 1e3
-    achieved_gbs = ffn_bytes / ffn_s / 1e9
-    achieved_tflops = ffn_flops / ffn_s / 1e12
+        na, nr = int(n_active[li, bi]), int(rows[li, bi])
+        win_bytes["up"] += na * (HF + shape.F) * s_w
+        win_bytes["down"] += na * (HF + shape.H) * s_w + ((2 * HF + shape.F + shape.H) * s_w if shape.residual else 0)
+        win_flops["up"] += 2 * HF * nr
+        win_flops["down"] += 2 * HF * nr + (4 * HF * shape.T if shape.residual else 0)
+    for d in evs:
+        for e in d.values():
+            hip.destroy(e)
+    kern = max(("up", "down"), key=lambda n: phase_ms[n])
+    k_s = phase_ms[kern] / 1e3
+    achieved_gbs = win_bytes[kern] / k_s / 1e9
+    achieved_tflops = win_flops[kern] / k_s / 1e12
     mean_active = float(n_active.mean())
     mean_rows = float(rows.mean())
     lay_b = layer_bytes(shape, mean_active)
@@ -199,11 +210,24 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    roof.update(kernel="expert FFN phase" if not shape.residual else "expert FFN + dense MLP phase",
-                avg_launch_us=round(phase_ms["ffn"] * 1e3 / args.steps, 2),
-                bytes_per_launch=int(ffn_bytes / args.steps),
-                unit_bytes=expert_unit_bytes(shape), units_per_launch=round(ffn_bytes / args.steps /
-                                                                           expert_unit_bytes(shape), 3))
+    unit_b = (HF + shape.F) * s_w if kern == "up" else (HF + shape.H) * s_w
+    roof.update(kernel=("expert W1 kernel (h = GeLU(x W1^T + b1))" if kern == "up"
+                        else "expert W2 kernel (y = h W2^T + b2)" + (" + dense MLP" if shape.residual else "")),
+                avg_launch_us=round(phase_ms[kern] * 1e3 / args.steps, 2),
+                bytes_per_launch=int(win_bytes[kern] / args.steps), unit="GB/s" if hbm_bound else "TFLOP/s",
+                unit_bytes=unit_b, units_per_launch=round(mean_active, 3),
+                ffn_phase={"us": round((phase_ms["up"] + phase_ms["down"]) * 1e3 / args.steps, 2),
+                           "GB/s": round((win_bytes["up"] + win_bytes["down"]) /
+                                         ((phase_ms["up"] + phase_ms["down"]) / 1e3) / 1e9, 1)})
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": METRIC,

@@ -72,7 +72,7 @@ typedef struct {
   int64_t num_tokens;          /* T >= 0 */
   int32_t hidden;              /* H, multiple of 64 */
   int32_t ffn;                 /* F (expert and dense-MLP width), multiple of 64 */
-  int32_t num_experts;         /* E >= 1: gate width and capacity denominator, <= 1024 */
+  int32_t num_experts;         /* E >= 1: gate width and capacity denominator, <= 512 */
   int32_t first_local_expert;  /* e_lo, 0 <= e_lo < E */
   int32_t num_local_experts;   /* E_loc >= 1, e_lo + E_loc <= E */
   int32_t top_k;               /* 1 or 2, <= E */
@@ -160,11 +160,13 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const moe_layer_weight
                                hipStream_t stream);
 
 /* Optional timing hook for moe_layer_forward_ex: any non-NULL event is recorded on
- * the stream right before / after the phase (gate, dispatch, expert FFN, combine). */
+ * the stream right before / after the phase (gate, dispatch, expert FFN, combine).
+ * ffn_split is recorded between the two expert kernels (after the W1 kernel, before
+ * the W2 kernel); the dense MLP of the residual mode runs after ffn_split. */
 typedef struct {
   hipEvent_t gate_begin, gate_end;
   hipEvent_t dispatch_begin, dispatch_end;
-  hipEvent_t ffn_begin, ffn_end;
+  hipEvent_t ffn_begin, ffn_split, ffn_end;
   hipEvent_t combine_begin, combine_end;
 } moe_phase_events_t;
 

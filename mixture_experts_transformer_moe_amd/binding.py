@@ -50,8 +50,8 @@ class LayerWeights(ctypes.Structure):
 
 class PhaseEvents(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("gate_begin", "gate_end", "dispatch_begin", "dispatch_end", "ffn_begin", "ffn_end",
-                 "combine_begin", "combine_end")]
+                ("gate_begin", "gate_end", "dispatch_begin", "dispatch_end", "ffn_begin", "ffn_split",
+                 "ffn_end", "combine_begin", "combine_end")]
 
 
 _lib = None

@@ -31,6 +31,12 @@ moe_status_t hip_fail(hipError_t e, const char* where) {
   return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+#define ST_TRY(expr)                 \
+  do {                               \
+    moe_status_t _s = (expr);        \
+    if (_s != MOE_OK) return _s;     \
+  } while (0)
+
 #define HIP_TRY(expr, where)                   \
   do {                                         \
     hipError_t _e = (expr);                    \
@@ -290,9 +296,12 @@ moe_status_t run_dispatch(const Plan& p, bool fuse_topk, const float* z, float* 
 
 // Expert FFN. x rows come from x via slot_token (a_rows != null) or from
 // x_disp directly. Decode path leaves partials in ws; GEMM path writes ydisp.
+moe_status_t record(hipEvent_t ev, hipStream_t s);
+
 moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const int* offsets,
                          const moe_layer_weights_t* w, float* ydisp, void* ws, hipStream_t s,
-                         void* y_fold = nullptr, const int* slot_token = nullptr, const float* topk_w = nullptr) {
+                         void* y_fold = nullptr, const int* slot_token = nullptr, const float* topk_w = nullptr,
+                         hipEvent_t split = nullptr) {
   if (p.exp_decode) {
     DecodeParams d{};
     d.x = x;
@@ -311,6 +320,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
     d.topk_w = topk_w;
     const int gsegs = (int)std::min<int64_t>(p.E_loc, p.R_max);
     HIP_TRY(launch_decode_up(p.dtype, p.exp_maxm, d, gsegs, s), "expert ffn up (decode)");
+    ST_TRY(record(split, s));
     HIP_TRY(launch_decode_down(p.dtype, p.exp_maxm, d, gsegs, y_fold != nullptr, s), "expert ffn down (decode)");
     return MOE_OK;
   }
@@ -336,6 +346,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g1.tile_count = cnt;
   g1.n_ntiles = nt1;
   HIP_TRY(launch_grouped_gemm(p.dtype, EPI_GELU, false, p.BM, p.BN1, g1, p.mt_bound * nt1, s), "expert gemm 1");
+  ST_TRY(record(split, s));
   GemmParams g2{};
   g2.A = h;
   g2.seg_off = offsets;
@@ -406,11 +417,6 @@ moe_status_t record(hipEvent_t ev, hipStream_t s) {
   return MOE_OK;
 }
 
-#define ST_TRY(expr)                 \
-  do {                               \
-    moe_status_t _s = (expr);        \
-    if (_s != MOE_OK) return _s;     \
-  } while (0)
 
 moe_status_t check_ws(const void* ws, size_t have, size_t need) {
   if (have < need)
@@ -565,7 +571,8 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   ST_TRY(record(e.dispatch_end, stream));
   ST_TRY(record(e.ffn_begin, stream));
   float* ydisp = wsp<float>(ws, p.o_ydisp);
-  if (p.R_max > 0) ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream, y_fold, slot_token, tw));
+  if (p.R_max > 0)
+    ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream, y_fold, slot_token, tw, e.ffn_split));
   float* dense = nullptr;
   if (p.residual) {
     dense = wsp<float>(ws, p.o_dense);

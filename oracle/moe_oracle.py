@@ -236,21 +236,28 @@ def layer_forward(x, weights: Mapping, *, E: int, k: int, cf: float, e_lo: int =
 
 def layer_rows(x_rows, token_slot_rows, w_rows, slot_expert: Sequence[int] | np.ndarray,
                expert_weights: Mapping[int, tuple], dense_weights: Optional[tuple] = None) -> np.ndarray:
-    """Output rows for a sample of tokens, given their routing.
+    """Output rows for a sample of tokens, given their routing (step 7 on a subset).
 
     x_rows [n, H]; token_slot_rows [n, k] (slot or -1); w_rows [n, k];
     slot_expert maps a slot to its local expert; expert_weights[e] =
     (w1, b1, w2, b2) for every local expert the sampled kept slots use.
+    Each expert's FFN runs once on the stack of sampled rows routed to it.
     """
     x_rows = _f64(x_rows)
     n, H = x_rows.shape
+    token_slot_rows = np.asarray(token_slot_rows)
     y = np.zeros((n, H))
     if dense_weights is not None:
         y += ffn(x_rows, *dense_weights)
+    uses = {}
     for i in range(n):
         for j in range(token_slot_rows.shape[1]):
             s = int(token_slot_rows[i, j])
             if s >= 0:
-                e = int(slot_expert[s])
-                y[i] += float(w_rows[i, j]) * ffn(x_rows[i:i + 1], *expert_weights[e])[0]
+                uses.setdefault(int(slot_expert[s]), []).append((i, j))
+    for e, ij in sorted(uses.items()):
+        rows = [i for i, _ in ij]
+        ye = ffn(x_rows[rows], *expert_weights[e])
+        for r, (i, j) in enumerate(ij):
+            y[i] += float(w_rows[i, j]) * ye[r]
     return y
