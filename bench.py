@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--batches", type=int, default=64, help="token batches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="skip the pass that times the expert kernels with launch-recorded events")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, copy a buffer of this size 3 times (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -146,6 +148,8 @@ def main():
     def step(i):
         layers[i % n_layers].forward(xs[(i // n_layers) % n_batches], y, stream)
 
+    print(f"[bench] inputs ready, routing stats taken ({n_layers} weight sets x {n_batches} batches)",
+          file=sys.stderr, flush=True)
     # ---- warmup, then exactly K timed steps
     for i in range(args.warmup):
         step(i)
@@ -164,6 +168,7 @@ def main():
     ms_per_step = ms_total / args.steps
     tokens_per_s = shape.T * args.steps / (ms_total / 1e3)
 
+    print(f"[bench] timed pass done: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
     # ---- second pass over the same K steps with per-phase HIP events (same stream):
     # gate, dispatch, the two expert kernels (W1 kernel "up", W2 kernel "down"), combine
     hip = _Hip()
@@ -195,8 +200,31 @@ def main():
     for d in evs:
         for e in d.values():
             hip.destroy(e)
-    kern = max(("up", "down"), key=lambda n: phase_ms[n])
-    k_s = phase_ms[kern] / 1e3
+    # ---- third pass: the expert kernels timed by their own dispatch (start / end
+    # timestamps of the launch itself, no queue packets between kernels)
+    kern_ms = {"up": phase_ms["up"], "down": phase_ms["down"]}
+    kernel_events = not args.no_kernel_events
+    if kernel_events:
+        kev = [{f: hip.event() for f in ("up_start", "up_stop", "down_start", "down_stop")} for _ in range(args.steps)]
+        for i in range(args.warmup):
+            step(i)
+        for i in range(args.steps):
+            pe = B.PhaseEvents(**{f: e.value for f, e in kev[i].items()})
+            layers[i % n_layers].forward(xs[(i // n_layers) % n_batches], y, stream, events=pe)
+        torch.cuda.synchronize()
+        kern_ms = {"up": 0.0, "down": 0.0}
+        for i in range(args.steps):
+            kern_ms["up"] += hip.elapsed_ms(kev[i]["up_start"], kev[i]["up_stop"])
+            kern_ms["down"] += hip.elapsed_ms(kev[i]["down_start"], kev[i]["down_stop"])
+        for d in kev:
+            for e in d.values():
+                hip.destroy(e)
+    # with the dense MLP (residual mode) the W2 window also holds the MLP kernels:
+    # there the phase-event window is the measured unit
+    if shape.residual:
+        kern_ms["down"] = phase_ms["down"]
+    kern = max(("up", "down"), key=lambda n: kern_ms[n])
+    k_s = kern_ms[kern] / 1e3
     achieved_gbs = win_bytes[kern] / k_s / 1e9
     achieved_tflops = win_flops[kern] / k_s / 1e12
     mean_active = float(n_active.mean())
@@ -213,12 +241,16 @@ def main():
     unit_b = (HF + shape.F) * s_w if kern == "up" else (HF + shape.H) * s_w
     roof.update(kernel=("expert W1 kernel (h = GeLU(x W1^T + b1))" if kern == "up"
                         else "expert W2 kernel (y = h W2^T + b2)" + (" + dense MLP" if shape.residual else "")),
-                avg_launch_us=round(phase_ms[kern] * 1e3 / args.steps, 2),
+                avg_launch_us=round(kern_ms[kern] * 1e3 / args.steps, 2),
+                timing=("kernel dispatch start/end events" if kernel_events and not (shape.residual and kern == "down")
+                        else "phase events around the kernel window"),
                 bytes_per_launch=int(win_bytes[kern] / args.steps), unit="GB/s" if hbm_bound else "TFLOP/s",
                 unit_bytes=unit_b, units_per_launch=round(mean_active, 3),
-                ffn_phase={"us": round((phase_ms["up"] + phase_ms["down"]) * 1e3 / args.steps, 2),
+                kernels_us={n: round(v * 1e3 / args.steps, 2) for n, v in kern_ms.items()},
+                ffn_phase={"us": round((kern_ms["up"] + kern_ms["down"]) * 1e3 / args.steps, 2),
                            "GB/s": round((win_bytes["up"] + win_bytes["down"]) /
-                                         ((phase_ms["up"] + phase_ms["down"]) / 1e3) / 1e9, 1)})
+                                         ((kern_ms["up"] + kern_ms["down"]) / 1e3) / 1e9, 1)})
+    roof["traffic"] = measured_traffic(shape.name, kern)
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20) // 2
@@ -254,9 +286,38 @@ def main():
                   "phase_us": {n: round(v * 1e3 / args.steps, 2) for n, v in phase_ms.items()},
                   "wall_s": round(wall, 3)},
     }
+    print("[bench] event passes done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights[0], xs, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources: the stored counter readings hold only while it matches."""
+    import hashlib
+    d = os.path.join(ROOT, "mixture_experts_transformer_moe_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kern: str):
+    """HBM bytes per launch of the kernel from the committed rocprofv3 counter
+    passes (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel reference), or None
+    when none were taken or the kernels changed since."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != kernel_source_digest() or kern not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][kern]
+    return {"read_bytes": k["read_bytes"], "write_bytes": k["write_bytes"],
+            "total_bytes": k["read_bytes"] + k["write_bytes"], "unit": "bytes per launch"}
 
 
 def cpu_baseline(shape, w, xs, budget_s: float) -> dict:

@@ -159,15 +159,19 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const moe_layer_weight
                                const void* x, void* y, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
-/* Optional timing hook for moe_layer_forward_ex: any non-NULL event is recorded on
- * the stream right before / after the phase (gate, dispatch, expert FFN, combine).
- * ffn_split is recorded between the two expert kernels (after the W1 kernel, before
- * the W2 kernel); the dense MLP of the residual mode runs after ffn_split. */
+/* Optional timing hook for moe_layer_forward_ex. Any non-NULL event of the first
+ * group is recorded on the stream right before / after the phase (gate, dispatch,
+ * expert FFN, combine); ffn_split is recorded between the two expert kernels (after
+ * the W1 kernel, before the W2 kernel; the residual mode's dense MLP runs after it).
+ * The second group is recorded by the launch of the expert kernels themselves
+ * (the dispatch's own start and end timestamps): up_* for the W1 kernel, down_*
+ * for the W2 kernel. Events must come from hipEventCreate (timing enabled). */
 typedef struct {
   hipEvent_t gate_begin, gate_end;
   hipEvent_t dispatch_begin, dispatch_end;
   hipEvent_t ffn_begin, ffn_split, ffn_end;
   hipEvent_t combine_begin, combine_end;
+  hipEvent_t up_start, up_stop, down_start, down_stop;
 } moe_phase_events_t;
 
 /* moe_layer_forward with phase events (ev may be NULL: then identical to it). */

@@ -51,7 +51,7 @@ class LayerWeights(ctypes.Structure):
 class PhaseEvents(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("gate_begin", "gate_end", "dispatch_begin", "dispatch_end", "ffn_begin", "ffn_split",
-                 "ffn_end", "combine_begin", "combine_end")]
+                 "ffn_end", "combine_begin", "combine_end", "up_start", "up_stop", "down_start", "down_stop")]
 
 
 _lib = None

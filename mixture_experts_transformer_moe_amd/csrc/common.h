@@ -1,10 +1,21 @@
 // Shared device/host helpers for the MoE layer kernels (gfx950 / CDNA4, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #define MOE_WAVE 64
+
+// Launch; when either event is given they are recorded by the dispatch itself
+// (kernel start / end timestamps, no extra queue packets).
+#define MOE_LAUNCH(kernel, grid, block, lds, stream, ev0, ev1, ...)                                  \
+  do {                                                                                              \
+    if ((ev0) || (ev1))                                                                             \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev0, ev1, 0, __VA_ARGS__);            \
+    else                                                                                            \
+      hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                            \
+  } while (0)
 
 namespace moe {
 
@@ -139,6 +150,7 @@ __device__ inline uint4 ld_nt16(const void* ptr) {
   return __builtin_bit_cast(uint4, v);
 }
 
+
 }  // namespace moe
 
 // ---------------------------------------------------------------------------
@@ -183,6 +195,22 @@ struct DecodeParams {
   void* out;              // down: fp32 [rows][H], or the layer output [T][H] when the combine is folded in
   const int* slot_token;  // folded combine: token of each row
   const float* topk_w;    // folded combine: top-1 weight of each token
+};
+
+// Routing of a decode-sized batch done inside the first expert kernel: every
+// work-group computes softmax / top-k and the dispatch of all k*T <= 256
+// assignments in LDS from the gate logits z; work-group 0 also writes them out.
+struct RouteParams {
+  const float* z;          // [T][E] gate logits
+  int T, k, E, e_lo, E_loc, C, R_max, renorm;
+  int* idx;                // [T][k]
+  float* w;                // [T][k]
+  int* demand;             // [E]
+  int* offsets;            // [E_loc + 1]
+  int* slot_token;         // [R_max]
+  int* token_slot;         // [T][k]
+  void* y_zero;            // output rows of tokens with nothing kept are zeroed (folded top-1 combine) or null
+  int y_esz;
 };
 
 }  // namespace moe

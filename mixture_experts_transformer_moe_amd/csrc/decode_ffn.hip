@@ -16,7 +16,9 @@
 // RPW x MAXM dot products. Work-group g x c takes the g-th non-empty segment
 // (found by each wave on its own from the offsets) and the c-th block of rows.
 #include "common.h"
+#include "dispatch_common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -118,24 +120,151 @@ __device__ inline float dot_rows(const uint4 (&wv)[RPW][NQ], const typename DT::
   return wave_reduce_multi<RPW * MAXM>(acc);
 }
 
+// Route a decode-sized batch (k*T <= 64) inside one work-group, entirely in LDS.
+// Top-k per token (one wave per token; work-group 0 also computes the softmax
+// weights), then, with one thread per assignment a (rank-major a = j*T + t):
+//   pos(a)  = earlier assignments to the same expert
+//   kept(a) = local expert and pos(a) < C
+//   slot(a) = kept assignments to lower local experts + pos(a)
+// which is the dispatch written out by direct counting (O(kT) per thread, no
+// scans). The g-th non-empty local expert is the g-th lowest expert among the
+// assignments with pos = 0 that are kept. Every work-group of the first expert
+// kernel does this for itself; work-group 0 also writes the routing out.
+#define UP_WAVES 8
+#define ROUTE_NTH (UP_WAVES * 64)
+#define ROUTE_MAX_KT 64
+__host__ __device__ inline size_t route_lds_ints(int T, int k, int R_max) {
+  return 5 * (size_t)T * k + R_max + 4;
+}
+
+// Returns false if this work-group's segment g does not exist; else seg, r0, r1
+// and lst (slot -> token, in LDS).
+__device__ inline bool route_tiny_lds(const RouteParams& rp, int H, int g, int* sh, int& seg, int& r0, int& r1,
+                                      const int*& lst_out) {
+  constexpr int NW = ROUTE_NTH / 64;
+  const int E = rp.E, T = rp.T, k = rp.k, kT = T * k;
+  int* lidx = sh;                                     // [T][k] chosen experts
+  float* lw = reinterpret_cast<float*>(lidx + kT);    // [T][k] weights (work-group 0)
+  int* lkey = reinterpret_cast<int*>(lw + kT);        // [kT] rank-major keys (E = none)
+  int* lpos = lkey + kT;                              // [kT] pos(a), or -1 when not kept
+  int* lslot = lpos + kT;                             // [kT] slot(a) or -1
+  int* lst = lslot + kT;                              // [R_max] slot -> token
+  int* sinfo = lst + rp.R_max;                        // seg, r0, r1, total
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const bool writer = blockIdx.x == 0;
+  for (int t = w; t < T; t += NW) {
+    if (writer) {
+      int sel[2];
+      wave_softmax_topk(rp.z + (long long)t * E, E, k, rp.renorm != 0, nullptr, lidx + t * k, lw + t * k, sel);
+    } else {
+      wave_topk_only(rp.z + (long long)t * E, E, k, lidx + t * k);
+    }
+  }
+  if (tid == 0) sinfo[0] = -1;
+  __syncthreads();
+  // keys in rank-major order
+  int key = E;
+  if (tid < kT) {
+    const int j = tid / T, t = tid - (tid / T) * T;
+    const int e = lidx[t * k + j];
+    key = (e >= 0 && e < E) ? e : E;
+    lkey[tid] = key;
+  }
+  __syncthreads();
+  const bool local = key >= rp.e_lo && key < rp.e_lo + rp.E_loc;
+  int pos = 0, cnt = 0;
+  if (tid < kT) {
+    for (int a = 0; a < kT; ++a) {
+      const int ka = lkey[a];
+      pos += (a < tid) & (ka == key);
+      cnt += ka == key;
+    }
+    lpos[tid] = (local && pos < rp.C) ? pos : -1;
+  }
+  __syncthreads();
+  if (tid < kT) {
+    int slot = -1;
+    if (lpos[tid] >= 0) {
+      int below = 0, rank = 0;
+      for (int a = 0; a < kT; ++a) {
+        const int ka = lkey[a];
+        const bool kept_a = lpos[a] >= 0;
+        below += kept_a & (ka < key);
+        rank += kept_a & (lpos[a] == 0) & (ka < key);
+      }
+      slot = below + pos;
+      lst[slot] = tid - (tid / T) * T;
+      if (pos == 0 && rank == g) {               // this assignment opens segment g
+        sinfo[0] = key - rp.e_lo;
+        sinfo[1] = below;
+        sinfo[2] = below + min(cnt, rp.C);
+      }
+    }
+    lslot[tid] = slot;
+  }
+  if (tid == 0) {
+    int total = 0;
+    for (int a = 0; a < kT; ++a) total += lpos[a] >= 0;
+    sinfo[3] = total;
+  }
+  __syncthreads();
+  if (writer) {
+    const int total = sinfo[3];
+    for (int a = tid; a < kT; a += ROUTE_NTH) {
+      const int j = a / T, t = a - (a / T) * T;
+      rp.idx[t * k + j] = lidx[t * k + j];
+      rp.w[t * k + j] = lw[t * k + j];
+      rp.token_slot[t * k + j] = lslot[a];
+    }
+    for (int e = tid; e < E; e += ROUTE_NTH) {
+      int c = 0;
+      for (int a = 0; a < kT; ++a) c += lkey[a] == e;
+      rp.demand[e] = c;
+    }
+    for (int i = tid; i <= rp.E_loc; i += ROUTE_NTH) {
+      int c = 0;
+      for (int a = 0; a < kT; ++a) c += (lpos[a] >= 0) & (lkey[a] < rp.e_lo + i);
+      rp.offsets[i] = c;
+    }
+    for (int s2 = tid; s2 < rp.R_max; s2 += ROUTE_NTH) rp.slot_token[s2] = s2 < total ? lst[s2] : -1;
+    if (rp.y_zero) {
+      for (int tt = tid; tt < T; tt += ROUTE_NTH) {
+        bool any = false;
+        for (int jj = 0; jj < k; ++jj) any |= lslot[jj * T + tt] >= 0;
+        if (!any) zero_dropped(rp.y_zero, rp.y_esz, tt, H);
+      }
+    }
+  }
+  seg = sinfo[0];
+  r0 = sinfo[1];
+  r1 = sinfo[2];
+  lst_out = lst;
+  return seg >= 0;
+}
+
 template <typename DT, int MAXM, int NQ>
-__global__ __launch_bounds__(256) void decode_up_kernel(DecodeParams p) {
+__global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p, RouteParams rp) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
   constexpr int N = RPW * MAXM;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nchunk = p.F / (4 * RPW);
+  const int nchunk = p.F / (UP_WAVES * RPW);
   const int g = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - g * nchunk;
+  const int* a_rows = p.a_rows;
   int seg = 0, r0 = 0, r1 = p.M;
-  if (p.seg_off) {
+  if (rp.z) {
+    extern __shared__ int route_sh[];
+    if (!route_tiny_lds(rp, p.H, g, route_sh, seg, r0, r1, a_rows)) return;
+  } else if (p.seg_off) {
     if (!find_active(p.seg_off, p.nseg, g, seg, r0, r1)) return;
   } else if (g > 0) {
     return;
   }
   const long long H = p.H, F = p.F;
-  const int f0 = chunk * 4 * RPW + wave * RPW;
+  const int f0 = chunk * UP_WAVES * RPW + wave * RPW;
   uint4 wv[RPW][NQ];
   load_rows<DT, NQ, RPW>(wv, reinterpret_cast<const T*>(p.w1) + (long long)seg * F * H + (long long)f0 * H, H);
   __builtin_amdgcn_sched_barrier(0);   // every weight load is in flight before anything else
@@ -145,7 +274,7 @@ __global__ __launch_bounds__(256) void decode_up_kernel(DecodeParams p) {
 #pragma unroll
   for (int m = 0; m < MAXM; ++m) {
     const int r = r0 + (m < M ? m : 0);
-    const long long row = p.a_rows ? (long long)p.a_rows[r] : (long long)r;
+    const long long row = a_rows ? (long long)a_rows[r] : (long long)r;
     act[m] = x + row * H;
   }
   const float s = dot_rows<DT, MAXM, NQ, RPW>(wv, act);
@@ -205,30 +334,38 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p) {
 // ---------------------------------------------------------------- launchers
 static int nq_of(int K, int vec) { return K / (64 * vec); }
 
+struct LaunchEv {
+  hipEvent_t start, stop;
+};
+
 template <typename DT, int MAXM, int NQ>
-static hipError_t launch_up_t(const DecodeParams& p, int grid_segs, hipStream_t s) {
+static hipError_t launch_up_t(const DecodeParams& p, const RouteParams& rp, int grid_segs, hipStream_t s,
+                              LaunchEv ev) {
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
-  const int grid = grid_segs * (p.F / (4 * RPW));
-  hipLaunchKernelGGL((decode_up_kernel<DT, MAXM, NQ>), dim3(grid), dim3(256), 0, s, p);
+  const int grid = grid_segs * (p.F / (UP_WAVES * RPW));
+  const size_t lds = rp.z ? sizeof(int) * route_lds_ints(rp.T, rp.k, rp.R_max) : 0;
+  MOE_LAUNCH((decode_up_kernel<DT, MAXM, NQ>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start, ev.stop, p, rp);
   return hipGetLastError();
 }
 
 template <typename DT, int MAXM, int NQ>
-static hipError_t launch_down_t(const DecodeParams& p, int grid_segs, bool fuse, hipStream_t s) {
+static hipError_t launch_down_t(const DecodeParams& p, int grid_segs, bool fuse, hipStream_t s, LaunchEv ev) {
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
   const int grid = grid_segs * (p.H / (4 * RPW));
-  if (fuse) hipLaunchKernelGGL((decode_down_kernel<DT, MAXM, NQ, true>), dim3(grid), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((decode_down_kernel<DT, MAXM, NQ, false>), dim3(grid), dim3(256), 0, s, p);
+  if (fuse) MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, true>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, p);
+  else MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, false>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, p);
   return hipGetLastError();
 }
 
 template <typename DT, int MAXM>
-static hipError_t launch_m(bool up, const DecodeParams& p, int grid_segs, bool fuse, hipStream_t s) {
+static hipError_t launch_m(bool up, const DecodeParams& p, const RouteParams& rp, int grid_segs, bool fuse,
+                           hipStream_t s, LaunchEv ev) {
   const int nq = up ? nq_of(p.H, DT::VEC) : nq_of(p.F, DT::VEC);
   switch (nq) {
-#define CASE(Q)                                                                              \
-  case Q:                                                                                    \
-    return up ? launch_up_t<DT, MAXM, Q>(p, grid_segs, s) : launch_down_t<DT, MAXM, Q>(p, grid_segs, fuse, s);
+#define CASE(Q)                                                                                      \
+  case Q:                                                                                            \
+    return up ? launch_up_t<DT, MAXM, Q>(p, rp, grid_segs, s, ev)                                    \
+              : launch_down_t<DT, MAXM, Q>(p, grid_segs, fuse, s, ev);
     CASE(1) CASE(2) CASE(4) CASE(8) CASE(16)
 #undef CASE
   }
@@ -236,12 +373,13 @@ static hipError_t launch_m(bool up, const DecodeParams& p, int grid_segs, bool f
 }
 
 template <typename DT>
-static hipError_t launch_dt(bool up, int maxm, const DecodeParams& p, int grid_segs, bool fuse, hipStream_t s) {
+static hipError_t launch_dt(bool up, int maxm, const DecodeParams& p, const RouteParams& rp, int grid_segs, bool fuse,
+                            hipStream_t s, LaunchEv ev) {
   switch (maxm) {
-    case 1: return launch_m<DT, 1>(up, p, grid_segs, fuse, s);
-    case 2: return launch_m<DT, 2>(up, p, grid_segs, fuse, s);
-    case 4: return launch_m<DT, 4>(up, p, grid_segs, fuse, s);
-    case 8: return launch_m<DT, 8>(up, p, grid_segs, fuse, s);
+    case 1: return launch_m<DT, 1>(up, p, rp, grid_segs, fuse, s, ev);
+    case 2: return launch_m<DT, 2>(up, p, rp, grid_segs, fuse, s, ev);
+    case 4: return launch_m<DT, 4>(up, p, rp, grid_segs, fuse, s, ev);
+    case 8: return launch_m<DT, 8>(up, p, rp, grid_segs, fuse, s, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -256,17 +394,27 @@ bool decode_supported(int dtype, int H, int F) {
   return ok(H) && ok(F);
 }
 
-hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s) {
+bool route_in_decode_supported(int T, int k, int E, int E_loc) {
+  return T * k <= ROUTE_MAX_KT && E_loc <= ROUTE_NTH && E <= 512;
+}
+
+hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s,
+                            hipEvent_t ev0, hipEvent_t ev1, const RouteParams* rp) {
   if (grid_segs <= 0) return hipSuccess;
-  return dtype == DT_F16 ? launch_dt<DtF16>(true, maxm, p, grid_segs, false, s)
-                         : launch_dt<DtBF16>(true, maxm, p, grid_segs, false, s);
+  const LaunchEv ev{ev0, ev1};
+  const RouteParams none{};
+  const RouteParams& r = rp ? *rp : none;
+  return dtype == DT_F16 ? launch_dt<DtF16>(true, maxm, p, r, grid_segs, false, s, ev)
+                         : launch_dt<DtBF16>(true, maxm, p, r, grid_segs, false, s, ev);
 }
 
 hipError_t launch_decode_down(int dtype, int maxm, const DecodeParams& p, int grid_segs, bool fuse_combine,
-                              hipStream_t s) {
+                              hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (grid_segs <= 0) return hipSuccess;
-  return dtype == DT_F16 ? launch_dt<DtF16>(false, maxm, p, grid_segs, fuse_combine, s)
-                         : launch_dt<DtBF16>(false, maxm, p, grid_segs, fuse_combine, s);
+  const LaunchEv ev{ev0, ev1};
+  const RouteParams none{};
+  return dtype == DT_F16 ? launch_dt<DtF16>(false, maxm, p, none, grid_segs, fuse_combine, s, ev)
+                         : launch_dt<DtBF16>(false, maxm, p, none, grid_segs, fuse_combine, s, ev);
 }
 
 }  // namespace moe

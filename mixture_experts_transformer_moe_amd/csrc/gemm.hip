@@ -302,45 +302,52 @@ hipError_t launch_gemm_plan(const int* seg_off, int nseg, int BM, int n_nt1, int
 }
 
 // ---------------------------------------------------------------- dispatch on shape
+struct LaunchEv {
+  hipEvent_t start, stop;
+};
+
 template <typename DT, int BM, int BN, int EPI, typename BiasT>
-static void launch_t(const GemmParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT>), dim3(grid), dim3(GEMM_THREADS), 0, s, p);
+static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
+  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT>), dim3(grid), dim3(GEMM_THREADS), 0, s, ev.start, ev.stop,
+             p);
 }
 
 template <typename DT, int BM, int BN>
-static void launch_epi(int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s) {
+static void launch_epi(int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   using T = typename DT::T;
-  if (epi == EPI_GELU) launch_t<DT, BM, BN, EPI_GELU, T>(p, grid, s);
-  else if (bias_f32) launch_t<DT, BM, BN, EPI_F32, float>(p, grid, s);
-  else launch_t<DT, BM, BN, EPI_F32, T>(p, grid, s);
+  if (epi == EPI_GELU) launch_t<DT, BM, BN, EPI_GELU, T>(p, grid, s, ev);
+  else if (bias_f32) launch_t<DT, BM, BN, EPI_F32, float>(p, grid, s, ev);
+  else launch_t<DT, BM, BN, EPI_F32, T>(p, grid, s, ev);
 }
 
 template <typename DT, int BN>
-static bool launch_bm(int BM, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s) {
+static bool launch_bm(int BM, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   switch (BM) {
-    case 16: launch_epi<DT, 16, BN>(epi, bias_f32, p, grid, s); return true;
-    case 32: launch_epi<DT, 32, BN>(epi, bias_f32, p, grid, s); return true;
-    case 64: launch_epi<DT, 64, BN>(epi, bias_f32, p, grid, s); return true;
-    case 128: launch_epi<DT, 128, BN>(epi, bias_f32, p, grid, s); return true;
+    case 16: launch_epi<DT, 16, BN>(epi, bias_f32, p, grid, s, ev); return true;
+    case 32: launch_epi<DT, 32, BN>(epi, bias_f32, p, grid, s, ev); return true;
+    case 64: launch_epi<DT, 64, BN>(epi, bias_f32, p, grid, s, ev); return true;
+    case 128: launch_epi<DT, 128, BN>(epi, bias_f32, p, grid, s, ev); return true;
   }
   return false;
 }
 
 template <typename DT>
-static bool launch_bn(int BM, int BN, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s) {
-  if (BN == 128) return launch_bm<DT, 128>(BM, epi, bias_f32, p, grid, s);
-  if (BN == 64) return launch_bm<DT, 64>(BM, epi, bias_f32, p, grid, s);
+static bool launch_bn(int BM, int BN, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s,
+                      LaunchEv ev) {
+  if (BN == 128) return launch_bm<DT, 128>(BM, epi, bias_f32, p, grid, s, ev);
+  if (BN == 64) return launch_bm<DT, 64>(BM, epi, bias_f32, p, grid, s, ev);
   return false;
 }
 
 hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN, const GemmParams& p, int grid,
-                               hipStream_t s) {
+                               hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (grid <= 0) return hipSuccess;
   bool ok;
+  const LaunchEv ev{ev0, ev1};
   switch (dtype) {
-    case DT_F32: ok = launch_bn<DtF32>(BM, BN, epi, bias_f32, p, grid, s); break;
-    case DT_F16: ok = launch_bn<DtF16>(BM, BN, epi, bias_f32, p, grid, s); break;
-    default: ok = launch_bn<DtBF16>(BM, BN, epi, bias_f32, p, grid, s); break;
+    case DT_F32: ok = launch_bn<DtF32>(BM, BN, epi, bias_f32, p, grid, s, ev); break;
+    case DT_F16: ok = launch_bn<DtF16>(BM, BN, epi, bias_f32, p, grid, s, ev); break;
+    default: ok = launch_bn<DtBF16>(BM, BN, epi, bias_f32, p, grid, s, ev); break;
   }
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();

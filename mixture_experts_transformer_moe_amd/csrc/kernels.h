@@ -36,14 +36,18 @@ enum { EPI_GELU = 0, EPI_F32 = 1 };
 hipError_t launch_gemm_plan(const int* seg_off, int nseg, int BM, int n_nt1, int n_nt2, int2* list1,
                             int2* list2, int* count, hipStream_t s);
 // bias_f32 selects a float bias (gate) instead of a dtype bias.
+// ev0 / ev1 (nullable): recorded by the kernel dispatch itself (start / end).
 hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN, const GemmParams& p,
-                               int grid, hipStream_t s);
+                               int grid, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // decode_ffn.hip
 bool decode_supported(int dtype, int H, int F);
-hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s);
+// rp (nullable): route the batch inside the kernel from the gate logits (see RouteParams).
+bool route_in_decode_supported(int T, int k, int E, int E_loc);
+hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, const RouteParams* rp = nullptr);
 hipError_t launch_decode_down(int dtype, int maxm, const DecodeParams& p, int grid_segs, bool fuse_combine,
-                              hipStream_t s);
+                              hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // combine.hip
 hipError_t launch_combine(int dtype, const float* ysrc, int P, long long prow, const int* token_slot,

@@ -100,6 +100,7 @@ struct Plan {
   // experts
   bool exp_decode;   // streaming kernels for segments of <= 8 rows, else grouped MFMA GEMM
   bool fold_combine; // top-1 standard layer on the decode path: the expert kernel writes y
+  bool route_in_up;  // decode path with a tiny batch: the first expert kernel does the dispatch
   int exp_maxm;
   int BM, BN1, BN2, mt_bound;
   // dense MLP
@@ -169,6 +170,7 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   p.exp_maxm = pow2_at_least(std::max<int64_t>(seg_rows, 1));
   p.exp_decode = seg_rows <= 8 && decode_supported(p.dtype, p.H, p.F);
   p.fold_combine = p.exp_decode && p.k == 1 && !p.residual;
+  p.route_in_up = p.exp_decode && route_in_decode_supported((int)p.T, p.k, p.E, p.E_loc);
   p.BM = gemm_bm_for_rows(seg_rows);
   p.BN1 = (p.F % 128 == 0) ? 128 : 64;
   p.BN2 = (p.H % 128 == 0) ? 128 : 64;
@@ -301,7 +303,10 @@ moe_status_t record(hipEvent_t ev, hipStream_t s);
 moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const int* offsets,
                          const moe_layer_weights_t* w, float* ydisp, void* ws, hipStream_t s,
                          void* y_fold = nullptr, const int* slot_token = nullptr, const float* topk_w = nullptr,
-                         hipEvent_t split = nullptr) {
+                         const moe_phase_events_t* ev = nullptr, const RouteParams* route = nullptr) {
+  const moe_phase_events_t none{};
+  const moe_phase_events_t& e = ev ? *ev : none;
+  hipEvent_t split = e.ffn_split;
   if (p.exp_decode) {
     DecodeParams d{};
     d.x = x;
@@ -319,9 +324,11 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
     d.slot_token = slot_token;
     d.topk_w = topk_w;
     const int gsegs = (int)std::min<int64_t>(p.E_loc, p.R_max);
-    HIP_TRY(launch_decode_up(p.dtype, p.exp_maxm, d, gsegs, s), "expert ffn up (decode)");
+    HIP_TRY(launch_decode_up(p.dtype, p.exp_maxm, d, gsegs, s, e.up_start, e.up_stop, route),
+            "expert ffn up (decode)");
     ST_TRY(record(split, s));
-    HIP_TRY(launch_decode_down(p.dtype, p.exp_maxm, d, gsegs, y_fold != nullptr, s), "expert ffn down (decode)");
+    HIP_TRY(launch_decode_down(p.dtype, p.exp_maxm, d, gsegs, y_fold != nullptr, s, e.down_start, e.down_stop),
+            "expert ffn down (decode)");
     return MOE_OK;
   }
   int2* l1 = wsp<int2>(ws, p.o_list1);
@@ -345,7 +352,8 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g1.tiles = l1;
   g1.tile_count = cnt;
   g1.n_ntiles = nt1;
-  HIP_TRY(launch_grouped_gemm(p.dtype, EPI_GELU, false, p.BM, p.BN1, g1, p.mt_bound * nt1, s), "expert gemm 1");
+  HIP_TRY(launch_grouped_gemm(p.dtype, EPI_GELU, false, p.BM, p.BN1, g1, p.mt_bound * nt1, s, e.up_start, e.up_stop),
+          "expert gemm 1");
   ST_TRY(record(split, s));
   GemmParams g2{};
   g2.A = h;
@@ -361,7 +369,9 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g2.tiles = l2;
   g2.tile_count = cnt;
   g2.n_ntiles = nt2;
-  HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, false, p.BM, p.BN2, g2, p.mt_bound * nt2, s), "expert gemm 2");
+  HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, false, p.BM, p.BN2, g2, p.mt_bound * nt2, s, e.down_start,
+                              e.down_stop),
+          "expert gemm 2");
   return MOE_OK;
 }
 
@@ -567,12 +577,35 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   ST_TRY(run_gate_logits(p, x, w->gate_w, w->gate_b, z, stream));
   ST_TRY(record(e.gate_end, stream));
   ST_TRY(record(e.dispatch_begin, stream));
-  ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot, y_fold, ws, stream));
+  RouteParams rp{};
+  if (p.route_in_up) {
+    // the first expert kernel routes the batch itself (every work-group in LDS)
+    rp.z = z;
+    rp.T = (int)p.T;
+    rp.k = p.k;
+    rp.E = p.E;
+    rp.e_lo = p.e_lo;
+    rp.E_loc = p.E_loc;
+    rp.C = (int)std::min<int64_t>(p.C, INT32_MAX);
+    rp.R_max = (int)p.R_max;
+    rp.renorm = p.renorm ? 1 : 0;
+    rp.idx = idx;
+    rp.w = tw;
+    rp.demand = demand;
+    rp.offsets = offsets;
+    rp.slot_token = slot_token;
+    rp.token_slot = token_slot;
+    rp.y_zero = y_fold;
+    rp.y_esz = (int)p.esz;
+  } else {
+    ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot, y_fold, ws, stream));
+  }
   ST_TRY(record(e.dispatch_end, stream));
   ST_TRY(record(e.ffn_begin, stream));
   float* ydisp = wsp<float>(ws, p.o_ydisp);
   if (p.R_max > 0)
-    ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream, y_fold, slot_token, tw, e.ffn_split));
+    ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream, y_fold, slot_token, tw, ev,
+                       p.route_in_up ? &rp : nullptr));
   float* dense = nullptr;
   if (p.residual) {
     dense = wsp<float>(ws, p.o_dense);

@@ -18,6 +18,45 @@ __device__ inline void wave_argmax(float& v, int& idx) {
   }
 }
 
+// The k largest logits (ties to the lower index) of a token whose logits this lane
+// holds in v[i] (expert lane + 64 i, i < epl). Every lane returns them in sel,
+// and the winning logits in bvs.
+__device__ inline void wave_select_topk(const float (&v)[MOE_MAX_EPL], int epl, int E, int k, int* sel, float* bvs) {
+  const int lane = lane_id();
+  sel[0] = sel[1] = -1;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_EPL; ++i) {
+      int e = lane + i * MOE_WAVE;
+      bool ok = (i < epl) && (e < E) && (e != sel[0]);
+      if (ok && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+    if (bi >= E) bi = (j == 0 ? 0 : (sel[0] == 0 ? 1 : 0));  // only if every logit is NaN
+    sel[j] = bi;
+    bvs[j] = bv;
+  }
+}
+
+// Only the top-k indices (no probabilities): the same choice as wave_softmax_topk.
+__device__ inline void wave_topk_only(const float* z, int E, int k, int* idx_out) {
+  const int lane = lane_id();
+  float v[MOE_MAX_EPL];
+  const int epl = (E + MOE_WAVE - 1) / MOE_WAVE;
+#pragma unroll
+  for (int i = 0; i < MOE_MAX_EPL; ++i) {
+    int e = lane + i * MOE_WAVE;
+    v[i] = (i < epl && e < E) ? z[e] : -INFINITY;
+  }
+  int sel[2];
+  float bvs[2];
+  wave_select_topk(v, epl, E, k, sel, bvs);
+  if (lane == 0)
+    for (int j = 0; j < k; ++j) idx_out[j] = sel[j];
+}
+
 // z: this token's E logits (fp32). Writes idx_out[0..k), w_out[0..k) and, when
 // probs != null, probs[0..E). Softmax is max-subtracted fp32; the choice is made
 // on the logits (ties to the lower expert index), so exp rounding cannot tie.
@@ -52,21 +91,9 @@ __device__ inline void wave_softmax_topk(const float* z, int E, int k, bool reno
     }
   }
   float wsel[2] = {0.f, 0.f};
-  sel[0] = sel[1] = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < MOE_MAX_EPL; ++i) {
-      int e = lane + i * MOE_WAVE;
-      bool ok = (i < epl) && (e < E) && (e != sel[0]);
-      if (ok && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
-    }
-    wave_argmax(bv, bi);
-    if (bi >= E) bi = (j == 0 ? 0 : (sel[0] == 0 ? 1 : 0));  // only if every logit is NaN
-    sel[j] = bi;
-    wsel[j] = expf(bv - m) * inv;
-  }
+  float bvs[2];
+  wave_select_topk(v, epl, E, k, sel, bvs);
+  for (int j = 0; j < k; ++j) wsel[j] = expf(bvs[j] - m) * inv;
   if (renorm) {
     float t = (k == 2) ? wsel[0] + wsel[1] : wsel[0];
     wsel[0] /= t;

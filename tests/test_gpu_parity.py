@@ -37,6 +37,8 @@ CASES = {
     "decode_f32_h256_k2": W.LayerShape("dec32b", T=5, H=256, F=256, E=16, E_loc=16, k=2, cf=2.0, dtype="f32"),
     "decode_k2_share": W.LayerShape("deck2", T=8, H=1024, F=2048, E=64, E_loc=16, e_lo=16, k=2, cf=1.0,
                                     dtype="f16"),
+    # streaming expert kernels fed by the dispatch kernel (batch too large to route in-kernel)
+    "decode_unrouted": W.LayerShape("decun", T=512, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
 }
 
 
