@@ -202,6 +202,7 @@ def main():
             hip.destroy(e)
     # ---- third pass: the expert kernels timed by their own dispatch (start / end
     # timestamps of the launch itself, no queue packets between kernels)
+    plan = B.moe_layer_plan(desc)
     kern_ms = {"up": phase_ms["up"], "down": phase_ms["down"]}
     kernel_events = not args.no_kernel_events
     if kernel_events:
@@ -238,9 +239,13 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    unit_b = (HF + shape.F) * s_w if kern == "up" else (HF + shape.H) * s_w
-    roof.update(kernel=("expert W1 kernel (h = GeLU(x W1^T + b1))" if kern == "up"
-                        else "expert W2 kernel (y = h W2^T + b2)" + (" + dense MLP" if shape.residual else "")),
+    if kern == "up":
+        unit_b = (HF + shape.F) * s_w
+        kname = "expert W1 kernel (h = GeLU(x W1^T + b1))"
+    else:
+        unit_b = (HF + shape.H) * s_w
+        kname = "expert W2 kernel (y = h W2^T + b2)" + (" + dense MLP" if shape.residual else "")
+    roof.update(kernel=kname,
                 avg_launch_us=round(kern_ms[kern] * 1e3 / args.steps, 2),
                 timing=("kernel dispatch start/end events" if kernel_events and not (shape.residual and kern == "down")
                         else "phase events around the kernel window"),
@@ -274,6 +279,7 @@ def main():
         "vs_baseline": None,
         "dtype": shape.dtype,
         "data": "synthetic",
+        "plan": plan,
         "config": {"workload": shape.name, "tokens": shape.T, "hidden": shape.H, "ffn": shape.F,
                    "experts": shape.E, "local_experts": shape.E_loc, "top_k": shape.k,
                    "capacity_factor": shape.cf, "mlp_type": shape.mlp_type, "weight_sets": n_layers,

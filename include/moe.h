@@ -108,6 +108,24 @@ int64_t moe_max_rows(const moe_layer_desc_t* d);
  * enough for every step entry point below. */
 moe_status_t moe_workspace_size(const moe_layer_desc_t* d, size_t* bytes /* host */);
 
+/* How moe_layer_forward runs a descriptor (host, pure). */
+typedef enum { MOE_GATE_VECTOR = 0, MOE_GATE_MATRIX = 1 } moe_gate_path_t;
+typedef enum {
+  MOE_EXPERTS_GROUPED_GEMM = 0,  /* matrix-core grouped GEMMs over the expert segments */
+  MOE_EXPERTS_STREAM = 1         /* segments of <= 8 rows: two weight-streaming kernels */
+} moe_expert_path_t;
+typedef struct {
+  int64_t capacity;              /* C */
+  int64_t max_rows;              /* R_max */
+  size_t workspace_bytes;
+  moe_gate_path_t gate_path;
+  moe_expert_path_t expert_path;
+  int32_t dispatch_in_expert_kernel;  /* 1: the first expert kernel routes the batch itself */
+  int32_t combine_in_expert_kernel;   /* 1: the last expert kernel writes y (top-1, standard) */
+  int32_t launches;                   /* kernel launches of one moe_layer_forward */
+} moe_layer_plan_t;
+moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out /* host */);
+
 /* Gate (steps z, p, idx, w above): x [T, H] dtype -> topk_idx [T, k] int32,
  * topk_w [T, k] fp32, and, when probs != NULL, probs [T, E] fp32. Logits,
  * softmax and the top-k choice are computed in fp32; ties go to the lower index.

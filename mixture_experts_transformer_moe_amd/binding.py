@@ -21,7 +21,7 @@ MOE_DTYPE_F32, MOE_DTYPE_F16, MOE_DTYPE_BF16 = 0, 1, 2
 MOE_MLP_STANDARD, MOE_MLP_RESIDUAL = 0, 1
 MOE_FLAG_RENORM_TOPK = 1
 
-EXPORTED = ["moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_gate", "moe_dispatch",
+EXPORTED = ["moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_layer_plan", "moe_gate", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_ffn", "moe_combine", "moe_layer_forward",
             "moe_layer_forward_ex", "moe_status_str", "moe_last_error"]
 
@@ -46,6 +46,16 @@ class LayerDesc(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("gate_w", "gate_b", "w1", "b1", "w2", "b2", "mlp_w1", "mlp_b1", "mlp_w2", "mlp_b2")]
+
+
+class LayerPlan(ctypes.Structure):
+    _fields_ = [("capacity", ctypes.c_int64), ("max_rows", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+                ("gate_path", ctypes.c_int), ("expert_path", ctypes.c_int),
+                ("dispatch_in_expert_kernel", ctypes.c_int32), ("combine_in_expert_kernel", ctypes.c_int32),
+                ("launches", ctypes.c_int32)]
+
+
+EXPERT_PATHS = {0: "grouped_gemm", 1: "stream"}
 
 
 class PhaseEvents(ctypes.Structure):
@@ -76,6 +86,8 @@ def lib() -> ctypes.CDLL:
         D = ctypes.POINTER(LayerDesc)
         W = ctypes.POINTER(LayerWeights)
         sz = ctypes.c_size_t
+        L.moe_layer_plan.restype = st
+        L.moe_layer_plan.argtypes = [D, ctypes.POINTER(LayerPlan)]
         L.moe_gate.restype = st
         L.moe_gate.argtypes = [D, P, P, P, P, P, P, P, sz, P]
         L.moe_dispatch.restype = st
@@ -165,6 +177,15 @@ def moe_workspace_size(desc: LayerDesc) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().moe_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
     return n.value
+
+
+def moe_layer_plan(desc: LayerDesc) -> dict:
+    pl = LayerPlan()
+    _check(lib().moe_layer_plan(ctypes.byref(desc), ctypes.byref(pl)))
+    return dict(capacity=pl.capacity, max_rows=pl.max_rows, workspace_bytes=pl.workspace_bytes,
+                gate_path="matrix" if pl.gate_path else "vector", expert_path=EXPERT_PATHS[pl.expert_path],
+                dispatch_in_expert_kernel=bool(pl.dispatch_in_expert_kernel),
+                combine_in_expert_kernel=bool(pl.combine_in_expert_kernel), launches=pl.launches)
 
 
 def _ws(ws: Optional[torch.Tensor]):

@@ -459,6 +459,22 @@ moe_status_t moe_workspace_size(const moe_layer_desc_t* d, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out) {
+  if (!out) return fail(MOE_ERR_INVALID_ARGUMENT, "out is NULL");
+  Plan p;
+  ST_TRY(validate(d, &p));
+  out->capacity = p.C;
+  out->max_rows = p.R_max;
+  out->workspace_bytes = p.total;
+  out->gate_path = p.gate_mfma ? MOE_GATE_MATRIX : MOE_GATE_VECTOR;
+  out->expert_path = p.exp_decode ? MOE_EXPERTS_STREAM : MOE_EXPERTS_GROUPED_GEMM;
+  out->dispatch_in_expert_kernel = p.route_in_up ? 1 : 0;
+  out->combine_in_expert_kernel = p.fold_combine ? 1 : 0;
+  out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) +
+                  (p.exp_decode ? 2 : 3) + (p.residual ? 2 : 0) + (p.fold_combine ? 0 : 1);
+  return MOE_OK;
+}
+
 moe_status_t moe_gate(const moe_layer_desc_t* d, const void* x, const void* gate_w, const float* gate_b,
                       int32_t* topk_idx, float* topk_w, float* probs, void* ws, size_t ws_bytes, hipStream_t stream) {
   Plan p;

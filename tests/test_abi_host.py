@@ -90,6 +90,32 @@ BAD = [
     (dict(E=1000), B.MOE_ERR_UNSUPPORTED),
 ]
 
+def test_layer_plan_paths():
+    """The plan names the path each benchmark layer takes and agrees with the
+    sizing calls."""
+    # launches: gate logits; softmax/top-k + count, scan, scatter (or none when
+    # the first expert kernel routes); the expert kernels (tile plan + two GEMMs,
+    # or two streaming kernels); the dense MLP's two; the combine unless folded
+    expect = {  # name: (gate, experts, dispatch in expert kernel, combine in expert kernel, launches)
+        "decode_350m_moe128": ("vector", "stream", True, True, 1 + 0 + 2 + 0),
+        "prefill_1p3b_moe128": ("matrix", "grouped_gemm", False, False, 1 + 4 + 3 + 1),
+        "prmoe_residual": ("matrix", "grouped_gemm", False, False, 1 + 4 + 3 + 2 + 1),
+        "share_24b_moe128": ("matrix", "grouped_gemm", False, False, 1 + 4 + 3 + 1),
+    }
+    for name, (gate, experts, disp, comb, launches) in expect.items():
+        shape = W.WORKLOADS[name]
+        d = B.desc_from_shape(shape)
+        pl = B.moe_layer_plan(d)
+        assert pl["capacity"] == oracle.capacity(shape.T, shape.E, shape.k, shape.cf)
+        assert pl["max_rows"] == B.moe_max_rows(d)
+        assert pl["workspace_bytes"] == B.moe_workspace_size(d)
+        got = (pl["gate_path"], pl["expert_path"], pl["dispatch_in_expert_kernel"], pl["combine_in_expert_kernel"],
+               pl["launches"])
+        assert got == (gate, experts, disp, comb, launches), (name, pl)
+    with pytest.raises(B.MoeError):
+        B.moe_layer_plan(B.make_desc(8, 1000, 4096, 128, 1, 1.0, "f16"))
+
+
 
 @pytest.mark.parametrize("kw,status", BAD, ids=[str(b[0]) for b in BAD])
 def test_invalid_descriptor(kw, status):
