@@ -411,6 +411,8 @@ hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid
 hipError_t launch_decode_down(int dtype, int maxm, const DecodeParams& p, int grid_segs, bool fuse_combine,
                               hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (grid_segs <= 0) return hipSuccess;
+  // the folded combine reads the row -> token map and the gate weights
+  if (fuse_combine && (!p.slot_token || !p.topk_w || !p.out)) return hipErrorInvalidValue;
   const LaunchEv ev{ev0, ev1};
   const RouteParams none{};
   return dtype == DT_F16 ? launch_dt<DtF16>(false, maxm, p, none, grid_segs, fuse_combine, s, ev)

@@ -10,7 +10,11 @@
 //
 // A work-group computes a BM x BN output tile with 4 waves; K advances 128 bytes
 // per stage through double-buffered LDS (row pitch 144 B: the 16 lanes of a
-// quarter-wave read 16 rows at distinct banks). Epilogues: bias + exact GeLU
+// quarter-wave read 16 rows at distinct banks). Global loads are full 128-byte
+// lines (8 lanes per row), which HBM serves faster than the 64-byte row pieces
+// the MFMA operand layout would need if loaded directly. Tiles of <= 64 rows
+// (bound by weight bandwidth) keep two stages of loads in flight in a register
+// ping-pong; 128-row tiles keep one. Epilogues: bias + exact GeLU
 // rounded to the I/O dtype (first expert GEMM), or bias in fp32 (second GEMM
 // and gate logits).
 //
@@ -76,8 +80,8 @@ __device__ inline float load_bias<_Float16>(const _Float16* b, int n) { return (
 template <>
 __device__ inline float load_bias<__bf16>(const __bf16* b, int n) { return (float)b[n]; }
 
-template <typename DT, int BM, int BN, int EPI, typename BiasT>
-__global__ __launch_bounds__(GEMM_THREADS) void grouped_gemm_kernel(GemmParams p) {
+template <typename DT, int BM, int BN, int EPI, typename BiasT, int DEPTH>
+__global__ __launch_bounds__(GEMM_THREADS, DEPTH) void grouped_gemm_kernel(GemmParams p) {
   using T = typename DT::T;
   constexpr int WM = (BM >= 64) ? 2 : 1;
   constexpr int WN = 4 / WM;
@@ -154,59 +158,108 @@ __global__ __launch_bounds__(GEMM_THREADS) void grouped_gemm_kernel(GemmParams p
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t ra[ACH], rb[BCH];
   const int nk = (int)(((long long)p.K * sizeof(T)) / 128);
   const int frag_row = lane & 15;
   const int frag_k = (lane >> 4) * 16;   // byte offset within a 64-byte k-block
 
-// global -> registers for stage KS (all loads of the stage in flight together)
-#define GEMM_GLOAD(KS)                                                                   \
+// global -> registers RA/RB for stage KS (all loads of the stage in flight together)
+#define GEMM_GLOAD(RA, RB, KS)                                                           \
   {                                                                                      \
     const long long off_ = (long long)(KS) * 128;                                        \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i) ra[i] =                              \
+    _Pragma("unroll") for (int i = 0; i < ACH; ++i) RA[i] =                              \
         *reinterpret_cast<const u32x4_t*>(a_src[i] + off_);                              \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i) rb[i] =                              \
+    _Pragma("unroll") for (int i = 0; i < BCH; ++i) RB[i] =                              \
         *reinterpret_cast<const u32x4_t*>(b_src[i] + off_);                              \
   }
-// registers -> LDS buffer BUF
-#define GEMM_LSTORE(BUF)                                                                 \
+// registers RA/RB -> LDS buffer BUF
+#define GEMM_LSTORE(RA, RB, BUF)                                                         \
   {                                                                                      \
     char* base_ = smem + (BUF) * STAGE;                                                  \
     _Pragma("unroll") for (int i = 0; i < ACH; ++i) if (a_own)                           \
-        *reinterpret_cast<u32x4_t*>(base_ + a_dst[i]) = ra[i];                           \
+        *reinterpret_cast<u32x4_t*>(base_ + a_dst[i]) = RA[i];                           \
     _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                      \
-        *reinterpret_cast<u32x4_t*>(base_ + b_dst[i]) = rb[i];                           \
+        *reinterpret_cast<u32x4_t*>(base_ + b_dst[i]) = RB[i];                           \
   }
+// MFMAs over the stage in LDS buffer BUF
+#define GEMM_MATH(BUF)                                                                   \
+  {                                                                                      \
+    const char* sb = smem + (BUF) * STAGE;                                               \
+    const char* sa = sb + BN * LDS_ROW;                                                  \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                   \
+      uint4 fa[TN], fb[TM];                                                              \
+      _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
+        fa[i] = *reinterpret_cast<const uint4*>(sb + (wave_n * TN * 16 + i * 16 + frag_row) * LDS_ROW + \
+                                                kb * 64 + frag_k);                       \
+      _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
+        fb[j] = *reinterpret_cast<const uint4*>(sa + (wave_m * TM * 16 + j * 16 + frag_row) * LDS_ROW + \
+                                                kb * 64 + frag_k);                       \
+      _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
+        _Pragma("unroll") for (int j = 0; j < TM; ++j) acc[i][j] = Mfma<DT>::op(fa[i], fb[j], acc[i][j]); \
+    }                                                                                    \
+  }
+#define GEMM_SB __builtin_amdgcn_sched_barrier(0)
 
-  GEMM_GLOAD(0);
-  GEMM_LSTORE(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) GEMM_GLOAD(ks + 1);
-    const char* sb = smem + buf * STAGE;
-    const char* sa = sb + BN * LDS_ROW;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      uint4 fa[TN], fb[TM];
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-        fa[i] = *reinterpret_cast<const uint4*>(sb + (wave_n * TN * 16 + i * 16 + frag_row) * LDS_ROW +
-                                                kb * 64 + frag_k);
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        fb[j] = *reinterpret_cast<const uint4*>(sa + (wave_m * TM * 16 + j * 16 + frag_row) * LDS_ROW +
-                                                kb * 64 + frag_k);
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = Mfma<DT>::op(fa[i], fb[j], acc[i][j]);
-    }
-    if (ks + 1 < nk) GEMM_LSTORE(buf ^ 1);
+  if constexpr (DEPTH == 1) {
+    // one stage in flight: stage ks + 1 loads while stage ks is multiplied
+    u32x4_t ra[ACH], rb[BCH];
+    GEMM_GLOAD(ra, rb, 0);
+    GEMM_LSTORE(ra, rb, 0);
     __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) {
+      const int buf = ks & 1;
+      if (ks + 1 < nk) GEMM_GLOAD(ra, rb, ks + 1);
+      GEMM_MATH(buf);
+      if (ks + 1 < nk) GEMM_LSTORE(ra, rb, buf ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // two stages in flight (register ping-pong): while stage c is multiplied from
+    // LDS, stages c + 1 and c + 2 are loading. Stage c sits in LDS buffer c & 1;
+    // stage c + 1 in register set (c + 1) & 1. The steady loop's loads are
+    // unconditional so the wait for one register set leaves the other in flight.
+    u32x4_t ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
+    GEMM_GLOAD(ra0, rb0, 0);
+    GEMM_SB;
+    if (nk > 1) GEMM_GLOAD(ra1, rb1, 1);
+    GEMM_SB;
+    GEMM_LSTORE(ra0, rb0, 0);
+    if (nk > 2) GEMM_GLOAD(ra0, rb0, 2);
+    GEMM_SB;
+    __syncthreads();
+    int c = 0;
+    for (; c + 4 < nk; c += 2) {   // LDS buf 0 = stage c, set 1 = stage c + 1, set 0 = stage c + 2
+      GEMM_MATH(0);
+      GEMM_LSTORE(ra1, rb1, 1);
+      GEMM_GLOAD(ra1, rb1, c + 3);
+      GEMM_SB;
+      __syncthreads();
+      GEMM_MATH(1);
+      GEMM_LSTORE(ra0, rb0, 0);
+      GEMM_GLOAD(ra0, rb0, c + 4);
+      GEMM_SB;
+      __syncthreads();
+    }
+    for (; c < nk; ++c) {          // the last (at most four) stages
+      if ((c & 1) == 0) {
+        GEMM_MATH(0);
+        if (c + 1 < nk) {
+          GEMM_LSTORE(ra1, rb1, 1);
+          if (c + 3 < nk) GEMM_GLOAD(ra1, rb1, c + 3);
+        }
+      } else {
+        GEMM_MATH(1);
+        if (c + 1 < nk) {
+          GEMM_LSTORE(ra0, rb0, 0);
+          if (c + 3 < nk) GEMM_GLOAD(ra0, rb0, c + 3);
+        }
+      }
+      __syncthreads();
+    }
   }
 #undef GEMM_GLOAD
 #undef GEMM_LSTORE
+#undef GEMM_MATH
+#undef GEMM_SB
 
   // ---- epilogue: lane holds D[n = 4*(lane/16) + q][m = lane % 16], q = 0..3
   const BiasT* bias = p.bias ? reinterpret_cast<const BiasT*>(p.bias) + (long long)seg * p.bias_stride : nullptr;
@@ -306,10 +359,14 @@ struct LaunchEv {
   hipEvent_t start, stop;
 };
 
+// Stages in flight: two for tiles of <= 64 rows (weight streaming, the register
+// budget allows it), one for 128-row tiles (more reuse per byte, and two would
+// cost occupancy).
 template <typename DT, int BM, int BN, int EPI, typename BiasT>
 static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
-  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT>), dim3(grid), dim3(GEMM_THREADS), 0, s, ev.start, ev.stop,
-             p);
+  constexpr int DEPTH = BM <= 64 ? 2 : 1;
+  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH>), dim3(grid), dim3(GEMM_THREADS), 0, s, ev.start,
+             ev.stop, p);
 }
 
 template <typename DT, int BM, int BN>

@@ -37,6 +37,11 @@ CASES = {
     "decode_f32_h256_k2": W.LayerShape("dec32b", T=5, H=256, F=256, E=16, E_loc=16, k=2, cf=2.0, dtype="f32"),
     "decode_k2_share": W.LayerShape("deck2", T=8, H=1024, F=2048, E=64, E_loc=16, e_lo=16, k=2, cf=1.0,
                                     dtype="f16"),
+    # grouped GEMM with two stages in flight (tiles of <= 64 rows): 64-wide column
+    # tiles (H = 320), bf16, and full 64-row tiles with top-2
+    "gemm_bn64": W.LayerShape("gbn64", T=256, H=320, F=512, E=16, E_loc=16, k=1, cf=1.0, dtype="f16"),
+    "gemm_bf16_bm32": W.LayerShape("gbf", T=512, H=512, F=1024, E=16, E_loc=16, k=1, cf=1.0, dtype="bf16"),
+    "gemm_bm64_k2": W.LayerShape("gk2", T=512, H=512, F=768, E=32, E_loc=32, k=2, cf=2.0, dtype="f16"),
     # streaming expert kernels fed by the dispatch kernel (batch too large to route in-kernel)
     "decode_unrouted": W.LayerShape("decun", T=512, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
 }
