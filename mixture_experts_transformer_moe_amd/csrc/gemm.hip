@@ -8,15 +8,19 @@
 // tile (rows m), so each lane of a 16x16 accumulator holds four consecutive n of
 // one output row: the epilogue stores 4 contiguous values per lane.
 //
-// A work-group computes a BM x BN output tile with 4 waves; K advances 128 bytes
-// per stage through double-buffered LDS (row pitch 144 B: the 16 lanes of a
-// quarter-wave read 16 rows at distinct banks). Global loads are full 128-byte
-// lines (8 lanes per row), which HBM serves faster than the 64-byte row pieces
-// the MFMA operand layout would need if loaded directly. Tiles of <= 64 rows
-// (bound by weight bandwidth) keep two stages of loads in flight in a register
-// ping-pong; 128-row tiles keep one. Epilogues: bias + exact GeLU
-// rounded to the I/O dtype (first expert GEMM), or bias in fp32 (second GEMM
-// and gate logits).
+// A work-group computes a BM x BN output tile with 4 waves (8 for the 256-wide
+// tiles of large segments); K advances 128 bytes per stage through
+// double-buffered LDS. In LDS each row keeps its 128 bytes as eight 16-byte
+// columns, column c of row r at position c ^ (r & 7): the row-wise stores and
+// the fragment reads (16 rows at one column) then hit distinct banks, where a
+// padded row pitch leaves every fragment read with bank conflicts. Global loads
+// are full 128-byte lines (8 lanes per row), which HBM serves faster than the
+// 64-byte row pieces the MFMA operand layout would need if loaded directly.
+// Tiles of <= 64 rows (bound by weight bandwidth) and the 128 x 256 tiles keep
+// two stages of loads in flight in a register ping-pong; 128 x 128 and
+// 160 x 256 tiles keep one (two would not fit the registers of two waves per
+// SIMD). Epilogues: bias + exact GeLU rounded to the I/O dtype (first expert
+// GEMM), or bias in fp32 (second GEMM and gate logits).
 //
 // Tiles come from a device tile list built by the plan kernel from the segment
 // offsets (no host sync): order is segment, then column tile, then m-tile, so
@@ -29,7 +33,7 @@
 namespace moe {
 
 #define GEMM_THREADS 256
-#define LDS_ROW 144      // bytes per LDS row: 128 bytes of K + 16 pad
+#define LDS_ROW 128      // bytes per LDS row: 128 bytes of K, 16-byte columns XOR-swizzled by row
 
 template <typename DT>
 struct Mfma;
@@ -80,28 +84,55 @@ __device__ inline float load_bias<_Float16>(const _Float16* b, int n) { return (
 template <>
 __device__ inline float load_bias<__bf16>(const __bf16* b, int n) { return (float)b[n]; }
 
-template <typename DT, int BM, int BN, int EPI, typename BiasT, int DEPTH>
-__global__ __launch_bounds__(GEMM_THREADS, DEPTH) void grouped_gemm_kernel(GemmParams p) {
+// Epilogue of a wave's TN x TM accumulator tiles: lane holds
+// D[n = n0 + 16 i + 4 (lane / 16) + q][m = m0 + 16 j + lane % 16], q = 0..3;
+// rows at or past r1 are not stored.
+template <typename DT, int EPI, typename BiasT, int TN, int TM>
+__device__ inline void gemm_epilogue(const GemmParams& p, const float4_t (&acc)[TN][TM], int seg, int n0, int m0,
+                                     int r1, int lane) {
   using T = typename DT::T;
-  constexpr int WM = (BM >= 64) ? 2 : 1;
-  constexpr int WN = 4 / WM;
-  constexpr int TN = BN / WN / 16;
-  constexpr int TM = BM / WM / 16;
-  static_assert(TN >= 1 && TM >= 1, "tile too small for 4 waves");
-  constexpr int ACH = (BM * 8 + GEMM_THREADS - 1) / GEMM_THREADS;   // 16-byte chunks per thread
-  constexpr int BCH = (BN * 8) / GEMM_THREADS;
-  static_assert(BCH >= 1, "BN too small");
-  constexpr int STAGE = (BN + BM) * LDS_ROW;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  const BiasT* bias = p.bias ? reinterpret_cast<const BiasT*>(p.bias) + (long long)seg * p.bias_stride : nullptr;
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    const int n = n0 + i * 16 + (lane >> 4) * 4;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bv[q] = load_bias<BiasT>(bias, n + q);
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int r = m0 + j * 16 + (lane & 15);
+      if (r >= r1) continue;
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] + bv[q];
+      if constexpr (EPI == EPI_GELU) {
+        T o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = DT::from_f(pin_f32(gelu_erf(v[q])));
+        T* dst = reinterpret_cast<T*>(p.C) + (long long)r * p.N + n;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[q] = o[q];
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(p.C) + (long long)r * p.N + n;
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
 
-  // ---- which tile
-  int nmt;
-  if (p.tiles) nmt = *p.tile_count;
-  else nmt = (p.M + BM - 1) / BM;
+// Which output tile a work-group computes: (segment, column tile, row tile) and
+// the segment's row range. Returns false past the end of the tile list.
+__device__ inline bool gemm_tile(const GemmParams& p, int BM, int& seg, int& nt, int& mt, int& r0, int& r1) {
+  const int nmt = p.tiles ? *p.tile_count : (p.M + BM - 1) / BM;
   const int total = nmt * p.n_ntiles;
-  if ((int)blockIdx.x >= total) return;
+  if ((int)blockIdx.x >= total) return false;
   const int L = xcd_remap(blockIdx.x, total);
-  int seg, nt, mt, r0, r1;
   if (p.tiles) {
     const int2 d = p.tiles[L];
     seg = d.x;
@@ -116,6 +147,30 @@ __global__ __launch_bounds__(GEMM_THREADS, DEPTH) void grouped_gemm_kernel(GemmP
     r0 = 0;
     r1 = p.M;
   }
+  return true;
+}
+
+// NTH threads (4 or 8 waves, laid out WM x WN over the tile); DEPTH stages of
+// global loads in flight; the launch bound asks for two waves per SIMD when the
+// registers of two stages or of eight waves must fit.
+template <typename DT, int BM, int BN, int EPI, typename BiasT, int DEPTH, int NTH>
+__global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped_gemm_kernel(GemmParams p) {
+  using T = typename DT::T;
+  constexpr int NW = NTH / 64;
+  constexpr int WM = (BM >= 64) ? 2 : 1;
+  constexpr int WN = NW / WM;
+  constexpr int TN = BN / WN / 16;
+  constexpr int TM = BM / WM / 16;
+  static_assert(TN >= 1 && TM >= 1 && TN * WN * 16 == BN && TM * WM * 16 == BM, "tile does not split over the waves");
+  constexpr int ACH = (BM * 8 + NTH - 1) / NTH;   // 16-byte chunks per thread
+  constexpr int BCH = (BN * 8) / NTH;
+  static_assert(BCH >= 1 && BCH * NTH == BN * 8, "BN does not split over the threads");
+  constexpr int STAGE = (BN + BM) * LDS_ROW;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  // ---- which tile
+  int seg, nt, mt, r0, r1;
+  if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) return;
   const int m0 = r0 + mt * BM;        // first row-space row of the tile
 
   const int tid = threadIdx.x;
@@ -124,32 +179,36 @@ __global__ __launch_bounds__(GEMM_THREADS, DEPTH) void grouped_gemm_kernel(GemmP
   const int wave_n = wave % WN;
   const int wave_m = wave / WN;
 
-  // ---- per-thread global source rows. With BM = 16 only half the threads own an
-  // activation chunk; the others load a valid duplicate and skip the LDS store,
-  // so every load is unconditional and all of them stay in flight together.
+  // ---- per-thread global source rows. LDS layout: row r of a stage holds its 128
+  // bytes of K as eight 16-byte columns, column c stored at position c ^ (r & 7),
+  // so both the row-wise stores (8 lanes per row) and the fragment reads (16 rows
+  // at one column) spread over all banks. When BM * 8 is not a multiple of the
+  // thread count, the threads past the tile load a valid duplicate and skip the
+  // LDS store, so every load is unconditional and all stay in flight together.
   const char* a_src[ACH];
   int a_dst[ACH];
+  bool a_own[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
-    const int c = min(tid + i * GEMM_THREADS, BM * 8 - 1);
+    a_own[i] = tid + i * NTH < BM * 8;
+    const int c = min(tid + i * NTH, BM * 8 - 1);
     const int row = c >> 3, col = c & 7;
     int r = m0 + row;
     if (r >= r1) r = r1 - 1;
     const long long arow = p.a_rows ? (long long)p.a_rows[r] : (long long)r;
     a_src[i] = reinterpret_cast<const char*>(p.A) + (arow * p.K) * (long long)sizeof(T) + col * 16;
-    a_dst[i] = BN * LDS_ROW + row * LDS_ROW + col * 16;
+    a_dst[i] = BN * LDS_ROW + row * LDS_ROW + ((col ^ (row & 7)) * 16);
   }
-  const bool a_own = (BM * 8 >= GEMM_THREADS) || (tid < BM * 8);
   const char* b_src[BCH];
   int b_dst[BCH];
   const char* bbase = reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
-    const int c = tid + i * GEMM_THREADS;
+    const int c = tid + i * NTH;
     const int row = c >> 3, col = c & 7;
     const long long n = (long long)nt * BN + row;
     b_src[i] = bbase + n * p.K * (long long)sizeof(T) + col * 16;
-    b_dst[i] = row * LDS_ROW + col * 16;
+    b_dst[i] = row * LDS_ROW + ((col ^ (row & 7)) * 16);
   }
 
   float4_t acc[TN][TM];
@@ -160,7 +219,9 @@ __global__ __launch_bounds__(GEMM_THREADS, DEPTH) void grouped_gemm_kernel(GemmP
 
   const int nk = (int)(((long long)p.K * sizeof(T)) / 128);
   const int frag_row = lane & 15;
-  const int frag_k = (lane >> 4) * 16;   // byte offset within a 64-byte k-block
+  // 16-byte column of the lane's fragment in k-block kb (0 or 1), swizzled for its row
+  const int frag_c0 = (((lane >> 4)) ^ (frag_row & 7)) * 16;
+  const int frag_c1 = ((4 + (lane >> 4)) ^ (frag_row & 7)) * 16;
 
 // global -> registers RA/RB for stage KS (all loads of the stage in flight together)
 #define GEMM_GLOAD(RA, RB, KS)                                                           \
@@ -175,7 +236,7 @@ __global__ __launch_bounds__(GEMM_THREADS, DEPTH) void grouped_gemm_kernel(GemmP
 #define GEMM_LSTORE(RA, RB, BUF)                                                         \
   {                                                                                      \
     char* base_ = smem + (BUF) * STAGE;                                                  \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i) if (a_own)                           \
+    _Pragma("unroll") for (int i = 0; i < ACH; ++i) if (a_own[i])                        \
         *reinterpret_cast<u32x4_t*>(base_ + a_dst[i]) = RA[i];                           \
     _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                      \
         *reinterpret_cast<u32x4_t*>(base_ + b_dst[i]) = RB[i];                           \
@@ -189,10 +250,10 @@ __global__ __launch_bounds__(GEMM_THREADS, DEPTH) void grouped_gemm_kernel(GemmP
       uint4 fa[TN], fb[TM];                                                              \
       _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
         fa[i] = *reinterpret_cast<const uint4*>(sb + (wave_n * TN * 16 + i * 16 + frag_row) * LDS_ROW + \
-                                                kb * 64 + frag_k);                       \
+                                                (kb ? frag_c1 : frag_c0));               \
       _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
         fb[j] = *reinterpret_cast<const uint4*>(sa + (wave_m * TM * 16 + j * 16 + frag_row) * LDS_ROW + \
-                                                kb * 64 + frag_k);                       \
+                                                (kb ? frag_c1 : frag_c0));               \
       _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
         _Pragma("unroll") for (int j = 0; j < TM; ++j) acc[i][j] = Mfma<DT>::op(fa[i], fb[j], acc[i][j]); \
     }                                                                                    \
@@ -261,40 +322,7 @@ __global__ __launch_bounds__(GEMM_THREADS, DEPTH) void grouped_gemm_kernel(GemmP
 #undef GEMM_MATH
 #undef GEMM_SB
 
-  // ---- epilogue: lane holds D[n = 4*(lane/16) + q][m = lane % 16], q = 0..3
-  const BiasT* bias = p.bias ? reinterpret_cast<const BiasT*>(p.bias) + (long long)seg * p.bias_stride : nullptr;
-#pragma unroll
-  for (int i = 0; i < TN; ++i) {
-    const int n = nt * BN + wave_n * TN * 16 + i * 16 + (lane >> 4) * 4;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bv[q] = load_bias<BiasT>(bias, n + q);
-    }
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int r = m0 + wave_m * TM * 16 + j * 16 + (lane & 15);
-      if (r >= r1) continue;
-      float v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] + bv[q];
-      if constexpr (EPI == EPI_GELU) {
-        T o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = DT::from_f(pin_f32(gelu_erf(v[q])));
-        T* dst = reinterpret_cast<T*>(p.C) + (long long)r * p.N + n;
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dst[q] = o[q];
-        }
-      } else {
-        float* dst = reinterpret_cast<float*>(p.C) + (long long)r * p.N + n;
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    }
-  }
+  gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + wave_m * TM * 16, r1, lane);
 }
 
 // ---------------------------------------------------------------- plan kernel
@@ -364,8 +392,9 @@ struct LaunchEv {
 // cost occupancy).
 template <typename DT, int BM, int BN, int EPI, typename BiasT>
 static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
-  constexpr int DEPTH = BM <= 64 ? 2 : 1;
-  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH>), dim3(grid), dim3(GEMM_THREADS), 0, s, ev.start,
+  constexpr int NTH = BN == 256 ? 512 : GEMM_THREADS;
+  constexpr int DEPTH = (BM <= 64 || (NTH == 512 && BM == 128)) ? 2 : 1;
+  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH>), dim3(grid), dim3(NTH), 0, s, ev.start,
              ev.stop, p);
 }
 
@@ -388,9 +417,22 @@ static bool launch_bm(int BM, int epi, bool bias_f32, const GemmParams& p, int g
   return false;
 }
 
+// 128 x 256 and 160 x 256 tiles, eight waves: segments of 65..320 rows and the dense MLP
+template <typename DT>
+static bool launch_big(int BM, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
+  switch (BM) {
+    case 128: launch_epi<DT, 128, 256>(epi, bias_f32, p, grid, s, ev); return true;
+    case 160: launch_epi<DT, 160, 256>(epi, bias_f32, p, grid, s, ev); return true;
+  }
+  return false;
+}
+
 template <typename DT>
 static bool launch_bn(int BM, int BN, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s,
                       LaunchEv ev) {
+  if constexpr (sizeof(typename DT::T) == 2) {
+    if (BN == 256) return launch_big<DT>(BM, epi, bias_f32, p, grid, s, ev);
+  }
   if (BN == 128) return launch_bm<DT, 128>(BM, epi, bias_f32, p, grid, s, ev);
   if (BN == 64) return launch_bm<DT, 64>(BM, epi, bias_f32, p, grid, s, ev);
   return false;

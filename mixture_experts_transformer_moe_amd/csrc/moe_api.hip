@@ -174,6 +174,13 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   p.BM = gemm_bm_for_rows(seg_rows);
   p.BN1 = (p.F % 128 == 0) ? 128 : 64;
   p.BN2 = (p.H % 128 == 0) ? 128 : 64;
+  // segments of more than 64 rows: eight-wave 128 x 256 or 160 x 256 tiles
+  // (160 when two of them cover a segment that would need three 128-row tiles)
+  const bool big_ok = p.dtype != MOE_DTYPE_F32 && p.F % 256 == 0 && p.H % 256 == 0;
+  if (p.BM == 128 && big_ok) {
+    p.BN1 = p.BN2 = 256;
+    if (seg_rows > 256 && seg_rows <= 320) p.BM = 160;
+  }
   {
     const int64_t segs = std::min<int64_t>(p.E_loc, p.R_max);
     const int64_t mtb = (p.R_max + (int64_t)(p.BM - 1) * segs) / p.BM;
@@ -184,8 +191,14 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   p.dense_maxm = pow2_at_least(std::max<int64_t>(p.T, 1));
   p.dense_decode = p.T <= 8 && decode_supported(p.dtype, p.H, p.F);
   p.dBM = gemm_bm_for_rows(p.T);
-  p.dBN1 = p.BN1;
-  p.dBN2 = p.BN2;
+  {
+    // 256-wide tiles only where they still give every CU two work-groups
+    const int64_t dmt = (p.T + p.dBM - 1) / p.dBM;
+    const bool big1 = p.dBM == 128 && big_ok && dmt * (p.F / 256) >= 512;
+    const bool big2 = p.dBM == 128 && big_ok && dmt * (p.H / 256) >= 512;
+    p.dBN1 = big1 ? 256 : ((p.F % 128 == 0) ? 128 : 64);
+    p.dBN2 = big2 ? 256 : ((p.H % 128 == 0) ? 128 : 64);
+  }
 
   // workspace layout
   size_t o = 0;

@@ -42,6 +42,10 @@ CASES = {
     "gemm_bn64": W.LayerShape("gbn64", T=256, H=320, F=512, E=16, E_loc=16, k=1, cf=1.0, dtype="f16"),
     "gemm_bf16_bm32": W.LayerShape("gbf", T=512, H=512, F=1024, E=16, E_loc=16, k=1, cf=1.0, dtype="bf16"),
     "gemm_bm64_k2": W.LayerShape("gk2", T=512, H=512, F=768, E=32, E_loc=32, k=2, cf=2.0, dtype="f16"),
+    # eight-wave 160 x 256 tiles: segments of up to C = 320 rows, two m-tiles each
+    "gemm_bm160": W.LayerShape("g160", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
+    "gemm_bm160_bf16_share": W.LayerShape("g160b", T=1024, H=512, F=1024, E=8, E_loc=4, e_lo=2, k=2, cf=1.25,
+                                          dtype="bf16"),
     # streaming expert kernels fed by the dispatch kernel (batch too large to route in-kernel)
     "decode_unrouted": W.LayerShape("decun", T=512, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
 }
