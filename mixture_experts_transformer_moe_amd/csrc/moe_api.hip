@@ -163,8 +163,12 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   p.nblk = dispatch_num_blocks(kT);
   // gate: matrix cores when the batch fills tiles; else 4x8 wave blocks on the ALUs
   p.gate_mfma = p.T >= 64 && (p.E % 64) == 0;
-  p.gate_BM = 64;
-  p.gate_BN = (p.E % 128 == 0) ? 128 : 64;
+  // 64 experts per column tile and the tallest row tile that still gives every
+  // CU two work-groups: the gate streams x once and is bound by that read
+  p.gate_BN = 64;
+  p.gate_BM = 16;
+  for (int bm : {64, 32})
+    if (((p.T + bm - 1) / bm) * (p.E / 64) >= 512) { p.gate_BM = bm; break; }
   // experts: streaming kernels for tiny segments, grouped MFMA GEMM otherwise
   const int64_t seg_rows = std::min<int64_t>(p.C, kT);
   p.exp_maxm = pow2_at_least(std::max<int64_t>(seg_rows, 1));
