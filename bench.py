@@ -298,28 +298,35 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the HIP sources: the stored counter readings hold only while it matches."""
+CSRC = os.path.join(ROOT, "mixture_experts_transformer_moe_amd", "csrc")
+# translation units of the measured kernels and what they include
+KERNEL_SOURCES = {
+    "decode": ["decode_ffn.hip", "common.h", "dispatch_common.h", "kernels.h", "topk.h"],
+    "gemm": ["gemm.hip", "common.h", "kernels.h"],
+}
+
+
+def kernel_source_digest(files) -> str:
+    """sha256 over the named HIP sources: stored counter readings hold only while it matches."""
     import hashlib
-    d = os.path.join(ROOT, "mixture_experts_transformer_moe_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in sorted(files):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
 def measured_traffic(workload: str, kern: str):
     """HBM bytes per launch of the kernel from the committed rocprofv3 counter
     passes (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel reference), or None
-    when none were taken or the kernels changed since."""
+    when none were taken or the kernel's sources changed since."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("source_sha256") != kernel_source_digest() or kern not in t.get("kernels", {}):
+    files = t.get("sources")
+    if not files or t.get("source_sha256") != kernel_source_digest(files) or kern not in t.get("kernels", {}):
         return None
     k = t["kernels"][kern]
     return {"read_bytes": k["read_bytes"], "write_bytes": k["write_bytes"],
