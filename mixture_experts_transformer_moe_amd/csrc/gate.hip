@@ -7,24 +7,29 @@
 
 namespace moe {
 
-// One 64-thread work-group (one wave) per block of 4 experts x 8 tokens, so the
-// gate weights stream through many CUs at once. NQ in {1, 2} (H = 64 * NQ * VEC):
-// every load of the block is issued before any arithmetic; NQ = 0: any H, with
-// gate_block's loop. Both forms accumulate and reduce in the same order.
-template <typename DT, int NQ>
+// One 64-thread work-group (one wave) per block of EB experts x 8 tokens, so the
+// gate weights stream through many CUs at once; small batches use EB = 1 or 2
+// (more work-groups, fewer dot products per lane: the kernel is latency-bound).
+// NQ in {1, 2} (H = 64 * NQ * VEC): every load of the block is issued before any
+// arithmetic; NQ = 0 (EB = 4): any H, with gate_block's loop. For a given EB the
+// accumulation and reduction order is fixed.
+template <typename DT, int NQ, int EB>
 __global__ __launch_bounds__(64) void gate_logits_fma_kernel(
     const typename DT::T* __restrict__ x, const typename DT::T* __restrict__ wg,
     const float* __restrict__ bias, float* __restrict__ z, int T, int H, int E) {
+  constexpr int NV = EB * GATE_TB;                 // logits per wave
+  constexpr int SH = 6 - (NV == 8 ? 3 : NV == 16 ? 4 : 5);
   const int lane = lane_id();
   const int t0 = blockIdx.x * GATE_TB;
-  const int e0 = blockIdx.y * GATE_EB;
+  const int e0 = blockIdx.y * EB;
   float r;
   if constexpr (NQ == 0) {
+    static_assert(EB == GATE_EB, "the looped form reduces 4 x 8 blocks");
     r = gate_block<DT>(wg, x, H, E, T, e0, t0);
   } else {
-    uint4 wv[GATE_EB][NQ], xv[GATE_TB][NQ];
+    uint4 wv[EB][NQ], xv[GATE_TB][NQ];
 #pragma unroll
-    for (int i = 0; i < GATE_EB; ++i)
+    for (int i = 0; i < EB; ++i)
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
         wv[i][q] = mask16(reinterpret_cast<const uint4*>(wg + (long long)min(e0 + i, E - 1) * H)[lane + 64 * q],
@@ -35,20 +40,22 @@ __global__ __launch_bounds__(64) void gate_logits_fma_kernel(
       for (int q = 0; q < NQ; ++q)
         xv[t][q] = mask16(reinterpret_cast<const uint4*>(x + (long long)min(t0 + t, T - 1) * H)[lane + 64 * q],
                           t0 + t < T);
-    float acc[GATE_EB * GATE_TB];
+    float acc[NV];
 #pragma unroll
-    for (int i = 0; i < GATE_EB * GATE_TB; ++i) acc[i] = 0.f;
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
-      for (int i = 0; i < GATE_EB; ++i)
+      for (int i = 0; i < EB; ++i)
 #pragma unroll
         for (int t = 0; t < GATE_TB; ++t) acc[i * GATE_TB + t] = dot16<DT>(wv[i][q], xv[t][q], acc[i * GATE_TB + t]);
-    r = wave_reduce_multi<GATE_EB * GATE_TB>(acc);
+    r = wave_reduce_multi<NV>(acc);
   }
-  const int e = e0 + gate_block_expert(lane);
-  const int t = t0 + gate_block_token(lane);
-  if ((lane & 1) == 0 && e < E && t < T) z[(long long)t * E + e] = r + (bias ? bias[e] : 0.f);
+  // after the reduction lane l holds logit number l >> SH: expert e0 + v / 8, token t0 + v % 8
+  const int v = lane >> SH;
+  const int e = e0 + v / GATE_TB;
+  const int t = t0 + (v % GATE_TB);
+  if ((lane & ((1 << SH) - 1)) == 0 && e < E && t < T) z[(long long)t * E + e] = r + (bias ? bias[e] : 0.f);
 }
 
 __global__ __launch_bounds__(256) void softmax_topk_kernel(const float* z, int T, int E,
@@ -62,21 +69,44 @@ __global__ __launch_bounds__(256) void softmax_topk_kernel(const float* z, int T
                     idx + (long long)t * k, w + (long long)t * k, sel);
 }
 
+template <typename DT, int EB>
+static hipError_t launch_gate_fma_eb(const void* x, const void* wg, const float* bias, float* z, int T, int H, int E,
+                                     int nq, hipStream_t s) {
+  using T_ = typename DT::T;
+  dim3 grid((T + GATE_TB - 1) / GATE_TB, (E + EB - 1) / EB);
+  if (nq == 1)
+    hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 1, EB>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg, bias,
+                       z, T, H, E);
+  else
+    hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 2, EB>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg, bias,
+                       z, T, H, E);
+  return hipGetLastError();
+}
+
+// experts per wave: 1 or 2 while that keeps the grid at <= 1024 / 2048 waves
+static int gate_experts_per_wave(int T, int E, int H, int dtype) {
+  const int vec = dtype == DT_F32 ? 4 : 8;
+  if (H % (64 * vec) != 0 || H / (64 * vec) > 2) return GATE_EB;
+  const long long tb = (T + GATE_TB - 1) / GATE_TB;
+  if (tb * E <= 1024) return 1;
+  if (tb * E <= 4096) return 2;
+  return GATE_EB;
+}
+
 template <typename DT>
 static hipError_t launch_gate_fma_t(const void* x, const void* wg, const float* bias, float* z, int T, int H, int E,
                                     hipStream_t s) {
   using T_ = typename DT::T;
-  dim3 grid((T + GATE_TB - 1) / GATE_TB, (E + GATE_EB - 1) / GATE_EB);
   const int nq = (H % (64 * DT::VEC) == 0) ? H / (64 * DT::VEC) : 0;
-  if (nq == 1)
-    hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 1>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg, bias, z,
-                       T, H, E);
-  else if (nq == 2)
-    hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 2>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg, bias, z,
-                       T, H, E);
-  else
-    hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 0>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg, bias, z,
-                       T, H, E);
+  const int eb = gate_experts_per_wave(T, E, H, sizeof(T_) == 4 ? DT_F32 : DT_F16);
+  if (nq == 1 || nq == 2) {
+    if (eb == 1) return launch_gate_fma_eb<DT, 1>(x, wg, bias, z, T, H, E, nq, s);
+    if (eb == 2) return launch_gate_fma_eb<DT, 2>(x, wg, bias, z, T, H, E, nq, s);
+    return launch_gate_fma_eb<DT, GATE_EB>(x, wg, bias, z, T, H, E, nq, s);
+  }
+  dim3 grid((T + GATE_TB - 1) / GATE_TB, (E + GATE_EB - 1) / GATE_EB);
+  hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 0, GATE_EB>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg,
+                     bias, z, T, H, E);
   return hipGetLastError();
 }
 

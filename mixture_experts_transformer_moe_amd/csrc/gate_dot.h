@@ -3,9 +3,8 @@
 // Every lane walks the hidden dimension in 16-byte vectors (vector c = lane,
 // lane + 64, ...), accumulating 32 fp32 dot products in a fixed order; one
 // multi-value wave reduction then leaves logit (e0 + (lane >> 4), t0 +
-// ((lane >> 1) & 7)) in each lane. The same routine serves the stand-alone
-// gate kernel and the fused decode gate+dispatch kernel, so both produce the
-// same bits.
+// ((lane >> 1) & 7)) in each lane. This is the looped form for hidden sizes that
+// are not 64 * 8 or 128 * 8 elements.
 #pragma once
 
 #include "common.h"
@@ -41,9 +40,5 @@ __device__ inline float gate_block(const typename DT::T* __restrict__ wg, const 
   (void)sizeof(T_);
   return wave_reduce_multi<GATE_EB * GATE_TB>(acc);
 }
-
-// Which logit a lane holds after gate_block (lanes with odd index repeat the even one).
-__device__ inline int gate_block_expert(int lane) { return lane >> 4; }
-__device__ inline int gate_block_token(int lane) { return (lane >> 1) & 7; }
 
 }  // namespace moe
