@@ -88,6 +88,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode_350m_moe128", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--stack", default=None, choices=sorted(W.STACKS),
+                    help="time a stack of MoE layers chained through their outputs instead of one layer")
     ap.add_argument("--layers", type=int, default=None, help="independent weight sets rotated per step")
     ap.add_argument("--batches", type=int, default=64, help="token batches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
@@ -106,6 +108,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.stack:
+        return run_stack(args)
     shape = W.WORKLOADS[args.workload]
     n_layers = args.layers if args.layers else (4 if shape.T <= 64 else 1)
     n_batches = args.batches if shape.T <= 64 else min(args.batches, 2)
@@ -295,6 +299,91 @@ def main():
     print("[bench] event passes done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights[0], xs, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def run_stack(args):
+    """A stack of MoE layers, each layer's output feeding the next; a step pushes
+    one token batch through every layer. Token batches rotate as in the
+    single-layer run; the algorithmic bytes of a step sum each layer's (active
+    experts, dense MLP, gate, x and y) with the active-expert counts read once,
+    outside the timed region, from the gate and dispatch entry points on the
+    chained inputs."""
+    shapes = W.STACKS[args.stack]
+    T = shapes[0].T
+    n_batches = args.batches if T <= 64 else min(args.batches, 2)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    layers = [B.MoELayer(sh, W.make_weights(sh, seed=i, device=dev)) for i, sh in enumerate(shapes)]
+    xs = [W.make_x(shapes[0], seed=1000 + b, device=dev) for b in range(n_batches)]
+    bufs = [torch.empty_like(xs[0]) for _ in range(2)]
+    torch.cuda.synchronize()
+
+    n_active = np.zeros((len(layers), n_batches), dtype=np.int64)
+    for bi in range(n_batches):
+        x = xs[bi]
+        for li, L in enumerate(layers):
+            sh = L.shape
+            R = max(B.moe_max_rows(L.desc), 1)
+            idx = torch.empty((T, sh.k), dtype=torch.int32, device=dev)
+            tw = torch.empty((T, sh.k), dtype=torch.float32, device=dev)
+            demand = torch.empty(sh.E, dtype=torch.int32, device=dev)
+            offsets = torch.empty(sh.E_loc + 1, dtype=torch.int32, device=dev)
+            st = torch.empty(R, dtype=torch.int32, device=dev)
+            ts = torch.empty((T, sh.k), dtype=torch.int32, device=dev)
+            B.moe_gate(L.desc, x, L.weights["gate_w"], L.weights["gate_b"], idx, tw, None, L.ws)
+            B.moe_dispatch(L.desc, idx, x, demand, offsets, st, ts, None, L.ws)
+            n_active[li, bi] = int((np.diff(offsets.cpu().numpy()) > 0).sum())
+            y = bufs[li % 2]
+            L.forward(x, y, stream)
+            x = y
+    torch.cuda.synchronize()
+
+    def step(i):
+        x = xs[i % n_batches]
+        for li, L in enumerate(layers):
+            L.forward(x, bufs[li % 2], stream)
+            x = bufs[li % 2]
+
+    print(f"[bench] stack {args.stack}: {len(layers)} layers ready, routing stats taken", file=sys.stderr,
+          flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    step_bytes = sum(layer_bytes(L.shape, float(n_active[li].mean())) for li, L in enumerate(layers))
+    gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+    out = {
+        "metric": "MoE-stack tokens/sec at 1 GPU (every layer of the stack per token)",
+        "value": round(T / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shapes[0].dtype,
+        "data": "synthetic",
+        "config": {"workload": args.stack, "layers": len(layers), "tokens": T, "hidden": shapes[0].H,
+                   "ffn": shapes[0].F, "experts": [sh.E for sh in shapes], "top_k": shapes[0].k,
+                   "capacity_factor": shapes[0].cf, "mlp_type": shapes[0].mlp_type, "token_batches": n_batches,
+                   "parallelism": "one GPU"},
+        "stack": {"us_per_layer": round(ms_per_step * 1e3 / len(layers), 2),
+                  "algorithmic_bytes_per_step": int(step_bytes),
+                  "mean_active_experts": [round(float(v), 2) for v in n_active.mean(axis=1)],
+                  "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4)}},
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -100,6 +100,30 @@ REDUCED = {
 }
 
 
+# Stacks of MoE layers run back to back, each layer's output feeding the next.
+# Shape: the 1.3B model of the pages' inference example (hidden 2048, 24 layers;
+# an MoE FFN every other layer gives 12 MoE layers), F = 4H, fp16.
+#   * Top2-MoE and Residual-MoE at equal shapes (64 experts): the two ways of
+#     giving each token two FFNs compared in the "Phenomenon2" part of the
+#     review's PR-MoE section (top-2 routing vs a fixed MLP plus one routed expert);
+#   * a PR-MoE pyramid: residual layers with more experts in the last layers
+#     (the pages fix only "more experts in the last few layers"; read here as
+#     32 experts in the first 10 MoE layers and 64 in the last 2).
+def _stack(name: str, T: int, experts, k: int, mlp_type: str):
+    return [LayerShape(f"{name}_l{i}", T=T, H=2048, F=8192, E=e, E_loc=e, k=k, cf=1.0, dtype="f16",
+                       mlp_type=mlp_type) for i, e in enumerate(experts)]
+
+
+_PYRAMID = [32] * 10 + [64] * 2
+STACKS = {
+    "top2_e64_decode": _stack("top2_e64_decode", 8, [64] * 12, 2, "standard"),
+    "residual_e64_decode": _stack("residual_e64_decode", 8, [64] * 12, 1, "residual"),
+    "prmoe_pyramid_decode": _stack("prmoe_pyramid_decode", 8, _PYRAMID, 1, "residual"),
+    "top2_e64_prefill": _stack("top2_e64_prefill", 2048, [64] * 12, 2, "standard"),
+    "residual_e64_prefill": _stack("residual_e64_prefill", 2048, [64] * 12, 1, "residual"),
+    "prmoe_pyramid_prefill": _stack("prmoe_pyramid_prefill", 2048, _PYRAMID, 1, "residual"),
+}
+
 def _mix64(*vals: int) -> int:
     """splitmix64 over a tuple of ints -> a 63-bit torch seed."""
     z = 0x9E3779B97F4A7C15

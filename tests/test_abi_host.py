@@ -183,3 +183,12 @@ def test_status_strings():
     for st, name in enumerate(["MOE_OK", "MOE_ERR_INVALID_ARGUMENT", "MOE_ERR_UNSUPPORTED",
                                "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_HIP"]):
         assert L.moe_status_str(st).decode() == name
+
+
+def test_bench_stacks_are_chainable():
+    """Every benchmark layer stack keeps one activation shape through its layers,
+    and every layer of it is a descriptor the library accepts."""
+    for name, shapes in W.STACKS.items():
+        assert len({(s.T, s.H, s.dtype) for s in shapes}) == 1, name
+        for s in shapes:
+            B.moe_layer_plan(B.desc_from_shape(s))
