@@ -178,6 +178,13 @@ struct GemmParams {
   const int2* tiles;      // tile list (seg, nt<<16 | mt) or null (single segment)
   const int* tile_count;  // number of m-tiles in the list (device)
   int n_ntiles;
+  // optional extra segment (id nseg) with its own operands: rows [0, M2) of A2
+  // (no row map), weights B2 [N][K], bias2 [N], output C2 [M2][N]; M2 = 0: none
+  const void* A2;
+  const void* B2;
+  const void* bias2;
+  void* C2;
+  int M2;
 };
 
 // Expert FFN for segments of at most MAXM rows: each work-group takes one

@@ -91,7 +91,11 @@ template <typename DT, int EPI, typename BiasT, int TN, int TM>
 __device__ inline void gemm_epilogue(const GemmParams& p, const float4_t (&acc)[TN][TM], int seg, int n0, int m0,
                                      int r1, int lane) {
   using T = typename DT::T;
-  const BiasT* bias = p.bias ? reinterpret_cast<const BiasT*>(p.bias) + (long long)seg * p.bias_stride : nullptr;
+  const bool extra = seg == p.nseg;
+  const void* bias_base = extra ? p.bias2 : p.bias;
+  void* Cout = extra ? p.C2 : p.C;
+  const BiasT* bias = bias_base ? reinterpret_cast<const BiasT*>(bias_base) + (extra ? 0 : (long long)seg * p.bias_stride)
+                                : nullptr;
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
     const int n = n0 + i * 16 + (lane >> 4) * 4;
@@ -111,7 +115,7 @@ __device__ inline void gemm_epilogue(const GemmParams& p, const float4_t (&acc)[
         T o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = DT::from_f(pin_f32(gelu_erf(v[q])));
-        T* dst = reinterpret_cast<T*>(p.C) + (long long)r * p.N + n;
+        T* dst = reinterpret_cast<T*>(Cout) + (long long)r * p.N + n;
         if constexpr (sizeof(T) == 2) {
           *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o);
         } else {
@@ -119,7 +123,7 @@ __device__ inline void gemm_epilogue(const GemmParams& p, const float4_t (&acc)[
           for (int q = 0; q < 4; ++q) dst[q] = o[q];
         }
       } else {
-        float* dst = reinterpret_cast<float*>(p.C) + (long long)r * p.N + n;
+        float* dst = reinterpret_cast<float*>(Cout) + (long long)r * p.N + n;
         *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
@@ -138,8 +142,13 @@ __device__ inline bool gemm_tile(const GemmParams& p, int BM, int& seg, int& nt,
     seg = d.x;
     nt = d.y >> 16;
     mt = d.y & 0xffff;
-    r0 = p.seg_off[seg];
-    r1 = p.seg_off[seg + 1];
+    if (seg == p.nseg) {       // the extra segment
+      r0 = 0;
+      r1 = p.M2;
+    } else {
+      r0 = p.seg_off[seg];
+      r1 = p.seg_off[seg + 1];
+    }
   } else {
     seg = 0;
     nt = L / nmt;
@@ -172,6 +181,7 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   int seg, nt, mt, r0, r1;
   if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) return;
   const int m0 = r0 + mt * BM;        // first row-space row of the tile
+  const bool extra = seg == p.nseg;   // the extra segment: its own operands, rows index A2 directly
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -195,13 +205,14 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
     const int row = c >> 3, col = c & 7;
     int r = m0 + row;
     if (r >= r1) r = r1 - 1;
-    const long long arow = p.a_rows ? (long long)p.a_rows[r] : (long long)r;
-    a_src[i] = reinterpret_cast<const char*>(p.A) + (arow * p.K) * (long long)sizeof(T) + col * 16;
+    const long long arow = (p.a_rows && !extra) ? (long long)p.a_rows[r] : (long long)r;
+    a_src[i] = reinterpret_cast<const char*>(extra ? p.A2 : p.A) + (arow * p.K) * (long long)sizeof(T) + col * 16;
     a_dst[i] = BN * LDS_ROW + row * LDS_ROW + ((col ^ (row & 7)) * 16);
   }
   const char* b_src[BCH];
   int b_dst[BCH];
-  const char* bbase = reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
+  const char* bbase = extra ? reinterpret_cast<const char*>(p.B2)
+                            : reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int c = tid + i * NTH;
@@ -326,9 +337,13 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 }
 
 // ---------------------------------------------------------------- plan kernel
+// Tile lists of the two expert GEMMs. An extra segment with mt_extra row tiles
+// (id nseg, e.g. the residual layer's dense MLP over all tokens) goes first, so
+// its tiles run alongside the expert tiles rather than after them.
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(const int* __restrict__ seg_off, int nseg, int BM,
                                                         int n_nt1, int n_nt2, int2* __restrict__ list1,
-                                                        int2* __restrict__ list2, int* __restrict__ count) {
+                                                        int2* __restrict__ list2, int* __restrict__ count,
+                                                        int mt_extra) {
   __shared__ int P[1025];
   __shared__ int C[1024];
   __shared__ int wsum[17];
@@ -354,11 +369,16 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(const int* __restrict__
   if (tid == 0) P[nseg] = wsum[16];
   __syncthreads();
   const int total = wsum[16];
-  if (tid == 0) count[0] = total;
+  if (tid == 0) count[0] = total + mt_extra;
   for (int g = 0; g < 2; ++g) {
     const int n_nt = g ? n_nt2 : n_nt1;
     int2* list = g ? list2 : list1;
     if (!list) continue;
+    const int n_extra = mt_extra * n_nt;
+    for (int L = tid; L < n_extra; L += 1024) {
+      const int nt = L / mt_extra, mt = L - nt * mt_extra;
+      list[L] = make_int2(nseg, (nt << 16) | mt);
+    }
     for (int L = tid; L < total * n_nt; L += 1024) {
       const int v = L / n_nt;
       int lo = 0, hi = nseg;               // largest s with P[s] <= v and P[s+1] > v
@@ -370,15 +390,15 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(const int* __restrict__
       const int q = L - P[s] * n_nt;
       const int cs = C[s];
       const int nt = q / cs, mt = q - (q / cs) * cs;
-      list[L] = make_int2(s, (nt << 16) | mt);
+      list[n_extra + L] = make_int2(s, (nt << 16) | mt);
     }
   }
 }
 
 hipError_t launch_gemm_plan(const int* seg_off, int nseg, int BM, int n_nt1, int n_nt2, int2* list1, int2* list2,
-                            int* count, hipStream_t s) {
+                            int* count, hipStream_t s, int mt_extra) {
   hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, seg_off, nseg, BM, n_nt1, n_nt2, list1, list2,
-                     count);
+                     count, mt_extra);
   return hipGetLastError();
 }
 

@@ -32,9 +32,10 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int* slot_token, i
 // gemm.hip
 enum { EPI_GELU = 0, EPI_F32 = 1 };
 // Tile list for segments [seg_off[s], seg_off[s+1]) with BM-row m-tiles, for two
-// GEMMs with n_nt1 / n_nt2 column tiles. count[0] = number of m-tiles.
+// GEMMs with n_nt1 / n_nt2 column tiles, preceded by mt_extra m-tiles of the
+// extra segment (id nseg, see GemmParams). count[0] = number of m-tiles.
 hipError_t launch_gemm_plan(const int* seg_off, int nseg, int BM, int n_nt1, int n_nt2, int2* list1,
-                            int2* list2, int* count, hipStream_t s);
+                            int2* list2, int* count, hipStream_t s, int mt_extra = 0);
 // bias_f32 selects a float bias (gate) instead of a dtype bias.
 // ev0 / ev1 (nullable): recorded by the kernel dispatch itself (start / end).
 hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN, const GemmParams& p,

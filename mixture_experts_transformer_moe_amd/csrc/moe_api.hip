@@ -105,6 +105,8 @@ struct Plan {
   int BM, BN1, BN2, mt_bound;
   // dense MLP
   bool dense_decode;
+  bool dense_in_experts;  // residual MLP as an extra segment of the expert GEMM launches
+  int mt_extra;           // its row tiles
   int dense_maxm, dBM, dBN1, dBN2;
   // workspace offsets (bytes)
   size_t o_z, o_idx, o_w, o_rank, o_blk, o_demand, o_off, o_slot_token, o_token_slot;
@@ -194,6 +196,19 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   }
   p.dense_maxm = pow2_at_least(std::max<int64_t>(p.T, 1));
   p.dense_decode = p.T <= 8 && decode_supported(p.dtype, p.H, p.F);
+  // GEMM path with 64-row expert tiles: the dense MLP's tiles join the expert
+  // GEMM launches (its L2-resident weights overlap the experts' weight
+  // streaming). With smaller expert tiles the MLP would run on tiles too thin
+  // for its T rows (measured slower), so it keeps its own launches.
+  p.dense_in_experts = p.residual && !p.exp_decode && !p.dense_decode && p.BM >= 64;
+  if (p.dense_in_experts) {
+    const int64_t mte = (p.T + p.BM - 1) / p.BM;
+    if (mte >= 65536) return fail(MOE_ERR_UNSUPPORTED, "too many row tiles");
+    p.mt_extra = (int)mte;
+    p.mt_bound += p.mt_extra;
+  }
+  if (!p.exp_decode && (int64_t)p.mt_bound * std::max(p.F / p.BN1, p.H / p.BN2) >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "too many tiles");
   p.dBM = gemm_bm_for_rows(p.T);
   {
     // 256-wide tiles only where they still give every CU two work-groups
@@ -320,7 +335,8 @@ moe_status_t record(hipEvent_t ev, hipStream_t s);
 moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const int* offsets,
                          const moe_layer_weights_t* w, float* ydisp, void* ws, hipStream_t s,
                          void* y_fold = nullptr, const int* slot_token = nullptr, const float* topk_w = nullptr,
-                         const moe_phase_events_t* ev = nullptr, const RouteParams* route = nullptr) {
+                         const moe_phase_events_t* ev = nullptr, const RouteParams* route = nullptr,
+                         bool with_dense = false) {
   const moe_phase_events_t none{};
   const moe_phase_events_t& e = ev ? *ev : none;
   hipEvent_t split = e.ffn_split;
@@ -352,7 +368,8 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   int2* l2 = wsp<int2>(ws, p.o_list2);
   int* cnt = wsp<int>(ws, p.o_count);
   const int nt1 = p.F / p.BN1, nt2 = p.H / p.BN2;
-  HIP_TRY(launch_gemm_plan(offsets, p.E_loc, p.BM, nt1, nt2, l1, l2, cnt, s), "gemm plan");
+  const bool dense = with_dense && p.dense_in_experts;
+  HIP_TRY(launch_gemm_plan(offsets, p.E_loc, p.BM, nt1, nt2, l1, l2, cnt, s, dense ? p.mt_extra : 0), "gemm plan");
   void* h = wsp<void>(ws, p.o_h);
   GemmParams g1{};
   g1.A = x;
@@ -369,6 +386,13 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g1.tiles = l1;
   g1.tile_count = cnt;
   g1.n_ntiles = nt1;
+  if (dense) {   // the residual MLP over all T tokens: h_dense = GeLU(x W1_mlp^T + b1_mlp)
+    g1.A2 = x;
+    g1.B2 = w->mlp_w1;
+    g1.bias2 = w->mlp_b1;
+    g1.C2 = wsp<void>(ws, p.o_dh);
+    g1.M2 = (int)p.T;
+  }
   HIP_TRY(launch_grouped_gemm(p.dtype, EPI_GELU, false, p.BM, p.BN1, g1, p.mt_bound * nt1, s, e.up_start, e.up_stop),
           "expert gemm 1");
   ST_TRY(record(split, s));
@@ -386,6 +410,13 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g2.tiles = l2;
   g2.tile_count = cnt;
   g2.n_ntiles = nt2;
+  if (dense) {   // m = h_dense W2_mlp^T + b2_mlp, fp32
+    g2.A2 = wsp<void>(ws, p.o_dh);
+    g2.B2 = w->mlp_w2;
+    g2.bias2 = w->mlp_b2;
+    g2.C2 = wsp<void>(ws, p.o_dense);
+    g2.M2 = (int)p.T;
+  }
   HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, false, p.BM, p.BN2, g2, p.mt_bound * nt2, s, e.down_start,
                               e.down_stop),
           "expert gemm 2");
@@ -488,7 +519,7 @@ moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out) {
   out->dispatch_in_expert_kernel = p.route_in_up ? 1 : 0;
   out->combine_in_expert_kernel = p.fold_combine ? 1 : 0;
   out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) +
-                  (p.exp_decode ? 2 : 3) + (p.residual ? 2 : 0) + (p.fold_combine ? 0 : 1);
+                  (p.exp_decode ? 2 : 3) + ((p.residual && !p.dense_in_experts) ? 2 : 0) + (p.fold_combine ? 0 : 1);
   return MOE_OK;
 }
 
@@ -636,13 +667,13 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   ST_TRY(record(e.dispatch_end, stream));
   ST_TRY(record(e.ffn_begin, stream));
   float* ydisp = wsp<float>(ws, p.o_ydisp);
-  if (p.R_max > 0)
+  if (p.R_max > 0 || p.dense_in_experts)
     ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream, y_fold, slot_token, tw, ev,
-                       p.route_in_up ? &rp : nullptr));
+                       p.route_in_up ? &rp : nullptr, true));
   float* dense = nullptr;
   if (p.residual) {
     dense = wsp<float>(ws, p.o_dense);
-    ST_TRY(run_dense(p, x, w, dense, ws, stream));
+    if (!p.dense_in_experts) ST_TRY(run_dense(p, x, w, dense, ws, stream));
   }
   ST_TRY(record(e.ffn_end, stream));
   ST_TRY(record(e.combine_begin, stream));
