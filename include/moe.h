@@ -122,7 +122,10 @@ typedef struct {
   moe_expert_path_t expert_path;
   int32_t dispatch_in_expert_kernel;  /* 1: the first expert kernel routes the batch itself */
   int32_t combine_in_expert_kernel;   /* 1: the last expert kernel writes y (top-1, standard) */
+  int32_t dense_in_expert_kernels;    /* 1: the residual MLP's tiles run inside the expert GEMMs */
   int32_t launches;                   /* kernel launches of one moe_layer_forward */
+  int32_t tile_rows;                  /* grouped GEMM: rows per tile (0 on the streaming path) */
+  int32_t tile_cols_w1, tile_cols_w2; /* grouped GEMM: columns per tile of the two products */
 } moe_layer_plan_t;
 moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out /* host */);
 
@@ -180,7 +183,9 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const moe_layer_weight
 /* Optional timing hook for moe_layer_forward_ex. Any non-NULL event of the first
  * group is recorded on the stream right before / after the phase (gate, dispatch,
  * expert FFN, combine); ffn_split is recorded between the two expert kernels (after
- * the W1 kernel, before the W2 kernel; the residual mode's dense MLP runs after it).
+ * the W1 kernel, before the W2 kernel). The residual mode's dense MLP runs inside
+ * the two expert GEMMs when moe_layer_plan reports dense_in_expert_kernels, else
+ * after the W2 kernel (inside the ffn_split .. ffn_end window).
  * The second group is recorded by the launch of the expert kernels themselves
  * (the dispatch's own start and end timestamps): up_* for the W1 kernel, down_*
  * for the W2 kernel. Events must come from hipEventCreate (timing enabled). */

@@ -52,7 +52,8 @@ class LayerPlan(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int64), ("max_rows", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("gate_path", ctypes.c_int), ("expert_path", ctypes.c_int),
                 ("dispatch_in_expert_kernel", ctypes.c_int32), ("combine_in_expert_kernel", ctypes.c_int32),
-                ("launches", ctypes.c_int32)]
+                ("dense_in_expert_kernels", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("tile_rows", ctypes.c_int32), ("tile_cols_w1", ctypes.c_int32), ("tile_cols_w2", ctypes.c_int32)]
 
 
 EXPERT_PATHS = {0: "grouped_gemm", 1: "stream"}
@@ -185,7 +186,9 @@ def moe_layer_plan(desc: LayerDesc) -> dict:
     return dict(capacity=pl.capacity, max_rows=pl.max_rows, workspace_bytes=pl.workspace_bytes,
                 gate_path="matrix" if pl.gate_path else "vector", expert_path=EXPERT_PATHS[pl.expert_path],
                 dispatch_in_expert_kernel=bool(pl.dispatch_in_expert_kernel),
-                combine_in_expert_kernel=bool(pl.combine_in_expert_kernel), launches=pl.launches)
+                combine_in_expert_kernel=bool(pl.combine_in_expert_kernel),
+                dense_in_expert_kernels=bool(pl.dense_in_expert_kernels), launches=pl.launches,
+                tile=(pl.tile_rows, pl.tile_cols_w1, pl.tile_cols_w2))
 
 
 def _ws(ws: Optional[torch.Tensor]):

@@ -50,9 +50,8 @@ hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid
 hipError_t launch_decode_down(int dtype, int maxm, const DecodeParams& p, int grid_segs, bool fuse_combine,
                               hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
-// combine.hip
-hipError_t launch_combine(int dtype, const float* ysrc, int P, long long prow, const int* token_slot,
-                          const float* w, int k, const float* dense, int Pd, void* y, int T, int H,
-                          hipStream_t s);
+// combine.hip: y[t] = sum_j w[t,j] ysrc[token_slot[t,j]] (+ dense[t]); ysrc [*, H], dense [T, H] fp32
+hipError_t launch_combine(int dtype, const float* ysrc, const int* token_slot, const float* w, int k,
+                          const float* dense, void* y, int T, int H, hipStream_t s);
 
 }  // namespace moe

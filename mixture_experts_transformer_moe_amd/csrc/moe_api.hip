@@ -518,6 +518,10 @@ moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out) {
   out->expert_path = p.exp_decode ? MOE_EXPERTS_STREAM : MOE_EXPERTS_GROUPED_GEMM;
   out->dispatch_in_expert_kernel = p.route_in_up ? 1 : 0;
   out->combine_in_expert_kernel = p.fold_combine ? 1 : 0;
+  out->dense_in_expert_kernels = p.dense_in_experts ? 1 : 0;
+  out->tile_rows = p.exp_decode ? 0 : p.BM;
+  out->tile_cols_w1 = p.exp_decode ? 0 : p.BN1;
+  out->tile_cols_w2 = p.exp_decode ? 0 : p.BN2;
   out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) +
                   (p.exp_decode ? 2 : 3) + ((p.residual && !p.dense_in_experts) ? 2 : 0) + (p.fold_combine ? 0 : 1);
   return MOE_OK;
@@ -607,8 +611,7 @@ moe_status_t moe_combine(const moe_layer_desc_t* d, const float* y_disp, const i
   PTR_TRY(y, "y");
   if (p.R_max > 0) PTR_TRY(y_disp, "y_disp");
   if (dense_out && !aligned16(dense_out)) return fail(MOE_ERR_INVALID_ARGUMENT, "dense_out is not 16-byte aligned");
-  HIP_TRY(launch_combine(p.dtype, y_disp, 1, p.R_max, token_slot, topk_w, p.k, dense_out, 1, y, (int)p.T, p.H,
-                         stream),
+  HIP_TRY(launch_combine(p.dtype, y_disp, token_slot, topk_w, p.k, dense_out, y, (int)p.T, p.H, stream),
           "combine");
   return MOE_OK;
 }
@@ -678,7 +681,7 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   ST_TRY(record(e.ffn_end, stream));
   ST_TRY(record(e.combine_begin, stream));
   if (!p.fold_combine)
-    HIP_TRY(launch_combine(p.dtype, ydisp, 1, p.R_max, token_slot, tw, p.k, dense, 1, y, (int)p.T, p.H, stream),
+    HIP_TRY(launch_combine(p.dtype, ydisp, token_slot, tw, p.k, dense, y, (int)p.T, p.H, stream),
             "combine");
   ST_TRY(record(e.combine_end, stream));
   return MOE_OK;

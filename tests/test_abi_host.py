@@ -113,6 +113,11 @@ def test_layer_plan_paths():
         got = (pl["gate_path"], pl["expert_path"], pl["dispatch_in_expert_kernel"], pl["combine_in_expert_kernel"],
                pl["launches"])
         assert got == (gate, experts, disp, comb, launches), (name, pl)
+        assert pl["dense_in_expert_kernels"] == (name == "prmoe_residual"), (name, pl)
+    # tiles: 64-row tiles for segments of <= 64 rows; 160 x 256 for the 24B share's 320-row segments
+    assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["prefill_1p3b_moe128"]))["tile"] == (64, 128, 128)
+    assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["share_24b_moe128"]))["tile"] == (160, 256, 256)
+    assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["decode_350m_moe128"]))["tile"] == (0, 0, 0)
     with pytest.raises(B.MoeError):
         B.moe_layer_plan(B.make_desc(8, 1000, 4096, 128, 1, 1.0, "f16"))
 
