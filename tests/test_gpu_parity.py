@@ -46,6 +46,16 @@ CASES = {
     "gemm_bm160": W.LayerShape("g160", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
     "gemm_bm160_bf16_share": W.LayerShape("g160b", T=1024, H=512, F=1024, E=8, E_loc=4, e_lo=2, k=2, cf=1.25,
                                           dtype="bf16"),
+    # edge cases: the maximum expert count (8 logits per lane in the top-k), a
+    # ragged token count (gate token blocks of 8), heavy drops (cf = 0.1), one
+    # token through a residual layer, and a share of a single local expert
+    "e512_decode": W.LayerShape("e512d", T=8, H=512, F=512, E=512, E_loc=512, k=2, cf=1.0, dtype="f16"),
+    "e512_gemm": W.LayerShape("e512g", T=600, H=256, F=512, E=512, E_loc=512, k=1, cf=4.0, dtype="f16"),
+    "ragged_t13": W.LayerShape("t13", T=13, H=512, F=1024, E=16, E_loc=16, k=2, cf=1.0, dtype="f16"),
+    "heavy_drop": W.LayerShape("drop", T=1000, H=256, F=512, E=8, E_loc=8, k=2, cf=0.1, dtype="f16"),
+    "residual_t1": W.LayerShape("rt1", T=1, H=512, F=1024, E=8, E_loc=8, k=1, cf=1.0, dtype="f16",
+                                mlp_type="residual"),
+    "share_eloc1": W.LayerShape("el1", T=256, H=256, F=512, E=16, E_loc=1, e_lo=5, k=2, cf=1.0, dtype="bf16"),
     # streaming expert kernels fed by the dispatch kernel (batch too large to route in-kernel)
     "decode_unrouted": W.LayerShape("decun", T=512, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
 }
