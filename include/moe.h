@@ -93,6 +93,19 @@ typedef struct {
   const void* mlp_b1;          /* residual only: [F] */
   const void* mlp_w2;          /* residual only: [H, F] */
   const void* mlp_b2;          /* residual only: [H] */
+  /* Optional per-expert placement, all four set or all NULL. Each is a DEVICE
+   * array of E_loc pointers: local expert i's W1 [F, H] starts at w1_experts[i],
+   * its b1 [F] at b1_experts[i], W2 [H, F] at w2_experts[i], b2 [H] at
+   * b2_experts[i]. A pointer may address device memory or pinned host memory
+   * (hipHostMalloc) that the device reads directly over the host link; the expert
+   * kernels read only the experts the routing selects. When set, w1 / b1 / w2 /
+   * b2 above are ignored and may be NULL. Every pointer must be 16-byte aligned
+   * and stay valid until the work enqueued with it has run (moe_expert_store_t
+   * below maintains such tables). */
+  const void* const* w1_experts;
+  const void* const* b1_experts;
+  const void* const* w2_experts;
+  const void* const* b2_experts;
 } moe_layer_weights_t;
 
 /* Capacity C = ceil(k * T * cf / E) (host, pure). The pages print no formula;
@@ -201,6 +214,53 @@ typedef struct {
 moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_weights_t* w,
                                   const void* x, void* y, void* ws, size_t ws_bytes,
                                   hipStream_t stream, const moe_phase_events_t* ev);
+
+/* ---- Host-resident experts with a device cache (for callers whose experts do
+ * not all fit in HBM). "[Review] DeepSpeed-MoE", PR-MoE / MoS section: the
+ * weights of the many experts are the memory cost of MoE inference; "Fast MoE
+ * Inference via Predictive Prefetching and Expert Replication": keep experts off
+ * the GPU and bring in the ones the routing selects.
+ *
+ * A store owns pinned host memory holding all E_loc local experts of one layer
+ * and `slots` device slots caching some of them, plus the per-expert pointer
+ * tables that moe_expert_store_weights() puts into a moe_layer_weights_t. The
+ * expert kernels read a cached expert from its slot and any other expert
+ * directly from pinned host memory over the host link, only when the routing
+ * selects it. create / destroy / set_expert synchronise the device (set-up
+ * calls); update only enqueues work. Use one store from one stream at a time. */
+typedef struct moe_expert_store* moe_expert_store_t;
+
+/* Allocates the store for descriptor d (pinned host memory for E_loc experts,
+ * `slots` in [0, E_loc] device slots). All experts start host-resident with
+ * zero weights; *out receives the handle (NULL on error). */
+moe_status_t moe_expert_store_create(const moe_layer_desc_t* d, int32_t slots, moe_expert_store_t* out /* host */);
+
+/* Frees everything the store owns (after a device synchronisation). NULL is a no-op. */
+moe_status_t moe_expert_store_destroy(moe_expert_store_t store);
+
+/* Copies local expert e's weights (HOST pointers, nn.Linear layout: W1 [F, H],
+ * b1 [F], W2 [H, F], b2 [H], dtype of the descriptor) into the store, and into
+ * its slot when it is cached. */
+moe_status_t moe_expert_store_set_expert(moe_expert_store_t store, int32_t e, const void* w1, const void* b1,
+                                         const void* w2, const void* b2);
+
+/* Points w's per-expert tables at the store (w1 / b1 / w2 / b2 are set to NULL;
+ * the caller fills the gate and, in residual mode, the dense MLP weights). */
+moe_status_t moe_expert_store_weights(moe_expert_store_t store, moe_layer_weights_t* w /* host */);
+
+/* Folds demand (HOST array [E] of assignments per global expert, e.g. a host
+ * copy of moe_dispatch's expert_demand) into each local expert's score
+ * (score = 0.5 * score + demand) and keeps the `slots` best-scoring experts
+ * (score > 0, ties to the lower index) in the device slots. Enqueued on stream:
+ * leaving experts switch to host reads, incoming experts are copied into their
+ * slots, then switch to slot reads; work enqueued earlier on the stream uses the
+ * old placement. *copied (may be NULL) receives the number of experts copied. */
+moe_status_t moe_expert_store_update(moe_expert_store_t store, const int32_t* demand /* host */,
+                                     hipStream_t stream, int32_t* copied /* host */);
+
+/* slot_of[i] (HOST array [E_loc]) = device slot of local expert i, or -1 if it
+ * is read from host memory, as of the last update call. */
+moe_status_t moe_expert_store_residency(moe_expert_store_t store, int32_t* slot_of /* host */);
 
 /* Static text for a status code. */
 const char* moe_status_str(moe_status_t st);

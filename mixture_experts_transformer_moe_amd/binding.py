@@ -11,6 +11,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,7 +24,9 @@ MOE_FLAG_RENORM_TOPK = 1
 
 EXPORTED = ["moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_layer_plan", "moe_gate", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_ffn", "moe_combine", "moe_layer_forward",
-            "moe_layer_forward_ex", "moe_status_str", "moe_last_error"]
+            "moe_layer_forward_ex", "moe_status_str", "moe_last_error",
+            "moe_expert_store_create", "moe_expert_store_destroy", "moe_expert_store_set_expert",
+            "moe_expert_store_weights", "moe_expert_store_update", "moe_expert_store_residency"]
 
 _DTYPE_CODE = {torch.float32: MOE_DTYPE_F32, torch.float16: MOE_DTYPE_F16, torch.bfloat16: MOE_DTYPE_BF16}
 _DTYPE_NAME = {"f32": MOE_DTYPE_F32, "f16": MOE_DTYPE_F16, "bf16": MOE_DTYPE_BF16}
@@ -45,7 +48,8 @@ class LayerDesc(ctypes.Structure):
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("gate_w", "gate_b", "w1", "b1", "w2", "b2", "mlp_w1", "mlp_b1", "mlp_w2", "mlp_b2")]
+                ("gate_w", "gate_b", "w1", "b1", "w2", "b2", "mlp_w1", "mlp_b1", "mlp_w2", "mlp_b2",
+                 "w1_experts", "b1_experts", "w2_experts", "b2_experts")]
 
 
 class LayerPlan(ctypes.Structure):
@@ -103,6 +107,18 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.argtypes = [D, W, P, P, P, sz, P]
         L.moe_layer_forward_ex.restype = st
         L.moe_layer_forward_ex.argtypes = [D, W, P, P, P, sz, P, ctypes.POINTER(PhaseEvents)]
+        L.moe_expert_store_create.restype = st
+        L.moe_expert_store_create.argtypes = [D, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_expert_store_destroy.restype = st
+        L.moe_expert_store_destroy.argtypes = [P]
+        L.moe_expert_store_set_expert.restype = st
+        L.moe_expert_store_set_expert.argtypes = [P, ctypes.c_int32, P, P, P, P]
+        L.moe_expert_store_weights.restype = st
+        L.moe_expert_store_weights.argtypes = [P, W]
+        L.moe_expert_store_update.restype = st
+        L.moe_expert_store_update.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_int32)]
+        L.moe_expert_store_residency.restype = st
+        L.moe_expert_store_residency.argtypes = [P, P]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_status_str.argtypes = [st]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -238,13 +254,67 @@ def moe_layer_forward_ex(desc, weights: LayerWeights, x, y, ws, stream=None, eve
                                       _stream(stream), ctypes.byref(events) if events is not None else None))
 
 
+class ExpertStore:
+    """moe_expert_store_t: every local expert in pinned host memory, `slots` of them
+    cached in device slots (argument marshalling only; the store is native)."""
+
+    def __init__(self, shape, slots: int):
+        self.shape = shape
+        self.desc = desc_from_shape(shape)
+        h = ctypes.c_void_p()
+        _check(lib().moe_expert_store_create(ctypes.byref(self.desc), int(slots), ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            _check(lib().moe_expert_store_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_expert(self, e: int, w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: torch.Tensor):
+        """Local expert e's weights from host tensors (contiguous, the layer's dtype)."""
+        ts = [t.detach().to("cpu").contiguous() for t in (w1, b1, w2, b2)]
+        _check(lib().moe_expert_store_set_expert(self.handle, int(e), *[t.data_ptr() for t in ts]))
+
+    def fill(self, weights: dict):
+        """All local experts from a weights dict of [E_loc, ...] tensors."""
+        for i in range(self.shape.E_loc):
+            self.set_expert(i, weights["w1"][i], weights["b1"][i], weights["w2"][i], weights["b2"][i])
+
+    def weights(self, weights: dict) -> LayerWeights:
+        """A LayerWeights with the gate / dense MLP of `weights` and the store's expert tables."""
+        cw = make_weights({k: v for k, v in weights.items() if k not in ("w1", "b1", "w2", "b2")})
+        _check(lib().moe_expert_store_weights(self.handle, ctypes.byref(cw)))
+        return cw
+
+    def update(self, demand, stream=None) -> int:
+        """Fold a host int32 demand vector [E] into the scores; returns experts copied."""
+        d = np.ascontiguousarray(np.asarray(demand, dtype=np.int32))
+        if d.shape != (self.shape.E,):
+            raise ValueError("demand must have one entry per global expert")
+        n = ctypes.c_int32(0)
+        _check(lib().moe_expert_store_update(self.handle, d.ctypes.data, _stream(stream), ctypes.byref(n)))
+        return n.value
+
+    def residency(self) -> np.ndarray:
+        out = np.zeros(self.shape.E_loc, dtype=np.int32)
+        _check(lib().moe_expert_store_residency(self.handle, out.ctypes.data))
+        return out
+
+
 class MoELayer:
     """One layer bound to its weights and a workspace (convenience for tests and the benchmark)."""
 
-    def __init__(self, shape, weights: dict, device="cuda"):
+    def __init__(self, shape, weights: dict, device="cuda", store: Optional["ExpertStore"] = None):
         self.shape = shape
         self.weights = weights
-        self.cw = make_weights(weights)
+        self.store = store
+        self.cw = store.weights(weights) if store is not None else make_weights(weights)
         self.desc = desc_from_shape(shape)
         self.ws = torch.empty(max(moe_workspace_size(self.desc), 16), dtype=torch.uint8, device=device)
 

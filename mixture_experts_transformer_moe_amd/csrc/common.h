@@ -174,6 +174,8 @@ struct GemmParams {
   long long b_stride;     // elements between consecutive segments' weights
   const void* bias;       // [nseg][N] or null
   long long bias_stride;
+  const void* const* Bp;     // optional: segment s's weights [N][K] at Bp[s] (replaces B, b_stride)
+  const void* const* biasp;  // optional: segment s's bias [N] at biasp[s] (replaces bias, bias_stride)
   void* C;                // output rows of the row space, ldc = N
   const int2* tiles;      // tile list (seg, nt<<16 | mt) or null (single segment)
   const int* tile_count;  // number of m-tiles in the list (device)
@@ -198,6 +200,9 @@ struct DecodeParams {
   int M;                  // rows when seg_off == null
   int H, F;
   const void* w1; const void* b1; const void* w2; const void* b2;  // [nseg][F][H], [nseg][F], ...
+  // optional per-segment placement: segment s's W1 [F][H] at w1p[s], ... (device
+  // arrays of nseg pointers, device or pinned host memory); null: the arrays above
+  const void* const* w1p; const void* const* b1p; const void* const* w2p; const void* const* b2p;
   void* h;                // hidden activation [rows][F], I/O dtype (written by up, read by down)
   void* out;              // down: fp32 [rows][H], or the layer output [T][H] when the combine is folded in
   const int* slot_token;  // folded combine: token of each row

@@ -266,7 +266,8 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p
   const long long H = p.H, F = p.F;
   const int f0 = chunk * UP_WAVES * RPW + wave * RPW;
   uint4 wv[RPW][NQ];
-  load_rows<DT, NQ, RPW>(wv, reinterpret_cast<const T*>(p.w1) + (long long)seg * F * H + (long long)f0 * H, H);
+  const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[seg]) : reinterpret_cast<const T*>(p.w1) + (long long)seg * F * H;
+  load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H, H);
   __builtin_amdgcn_sched_barrier(0);   // every weight load is in flight before anything else
   const int M = min(r1 - r0, MAXM);
   const T* x = reinterpret_cast<const T*>(p.x);
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p
   const int v = lane >> SH;
   const int i = v / MAXM, m = v - (v / MAXM) * MAXM;
   if ((lane & ((1 << SH) - 1)) == 0 && m < M) {
-    const T* b1 = reinterpret_cast<const T*>(p.b1) + (long long)seg * F;
+    const T* b1 = p.b1p ? reinterpret_cast<const T*>(p.b1p[seg]) : reinterpret_cast<const T*>(p.b1) + (long long)seg * F;
     const float u = s + DT::to_f(b1[f0 + i]);
     reinterpret_cast<T*>(p.h)[(long long)(r0 + m) * F + f0 + i] = DT::from_f(pin_f32(gelu_erf(u)));
   }
@@ -307,7 +308,8 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p) {
   const long long H = p.H, F = p.F;
   const int j0 = chunk * 4 * RPW + wave * RPW;
   uint4 wv[RPW][NQ];
-  load_rows<DT, NQ, RPW>(wv, reinterpret_cast<const T*>(p.w2) + (long long)seg * H * F + (long long)j0 * F, F);
+  const T* w2s = p.w2p ? reinterpret_cast<const T*>(p.w2p[seg]) : reinterpret_cast<const T*>(p.w2) + (long long)seg * H * F;
+  load_rows<DT, NQ, RPW>(wv, w2s + (long long)j0 * F, F);
   __builtin_amdgcn_sched_barrier(0);
   const int M = min(r1 - r0, MAXM);
   const T* h = reinterpret_cast<const T*>(p.h);
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p) {
   const int v = lane >> SH;
   const int i = v / MAXM, m = v - (v / MAXM) * MAXM;
   if ((lane & ((1 << SH) - 1)) == 0 && m < M) {
-    const T* b2 = reinterpret_cast<const T*>(p.b2) + (long long)seg * H;
+    const T* b2 = p.b2p ? reinterpret_cast<const T*>(p.b2p[seg]) : reinterpret_cast<const T*>(p.b2) + (long long)seg * H;
     const float yv = s + DT::to_f(b2[j0 + i]);
     if (FUSE) {
       const int t = p.slot_token[r0 + m];

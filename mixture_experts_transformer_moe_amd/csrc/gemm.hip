@@ -92,9 +92,10 @@ __device__ inline void gemm_epilogue(const GemmParams& p, const float4_t (&acc)[
                                      int r1, int lane) {
   using T = typename DT::T;
   const bool extra = seg == p.nseg;
-  const void* bias_base = extra ? p.bias2 : p.bias;
   void* Cout = extra ? p.C2 : p.C;
-  const BiasT* bias = bias_base ? reinterpret_cast<const BiasT*>(bias_base) + (extra ? 0 : (long long)seg * p.bias_stride)
+  const BiasT* bias = extra     ? reinterpret_cast<const BiasT*>(p.bias2)
+                      : p.biasp ? reinterpret_cast<const BiasT*>(p.biasp[seg])
+                      : p.bias  ? reinterpret_cast<const BiasT*>(p.bias) + (long long)seg * p.bias_stride
                                 : nullptr;
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
@@ -211,8 +212,9 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   }
   const char* b_src[BCH];
   int b_dst[BCH];
-  const char* bbase = extra ? reinterpret_cast<const char*>(p.B2)
-                            : reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
+  const char* bbase = extra    ? reinterpret_cast<const char*>(p.B2)
+                      : p.Bp ? reinterpret_cast<const char*>(p.Bp[seg])
+                             : reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int c = tid + i * NTH;

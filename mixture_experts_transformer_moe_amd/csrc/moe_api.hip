@@ -11,6 +11,7 @@
 #include "moe.h"
 #include "common.h"
 #include "kernels.h"
+#include "api_internal.h"
 
 using namespace moe;
 
@@ -271,10 +272,21 @@ moe_status_t check_ptr(const void* p, const char* name) {
 moe_status_t check_weights(const Plan& p, const moe_layer_weights_t* w, bool experts, bool dense) {
   if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "weights is NULL");
   if (experts) {
-    PTR_TRY(w->w1, "w1");
-    PTR_TRY(w->b1, "b1");
-    PTR_TRY(w->w2, "w2");
-    PTR_TRY(w->b2, "b2");
+    const int tables = (w->w1_experts != nullptr) + (w->b1_experts != nullptr) + (w->w2_experts != nullptr) +
+                       (w->b2_experts != nullptr);
+    if (tables == 4) {
+      PTR_TRY(w->w1_experts, "w1_experts");
+      PTR_TRY(w->b1_experts, "b1_experts");
+      PTR_TRY(w->w2_experts, "w2_experts");
+      PTR_TRY(w->b2_experts, "b2_experts");
+    } else if (tables != 0) {
+      return fail(MOE_ERR_INVALID_ARGUMENT, "set all four per-expert pointer tables or none");
+    } else {
+      PTR_TRY(w->w1, "w1");
+      PTR_TRY(w->b1, "b1");
+      PTR_TRY(w->w2, "w2");
+      PTR_TRY(w->b2, "b2");
+    }
   }
   if (dense) {
     PTR_TRY(w->mlp_w1, "mlp_w1");
@@ -352,6 +364,10 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
     d.b1 = w->b1;
     d.w2 = w->w2;
     d.b2 = w->b2;
+    d.w1p = w->w1_experts;
+    d.b1p = w->b1_experts;
+    d.w2p = w->w2_experts;
+    d.b2p = w->b2_experts;
     d.h = wsp<void>(ws, p.o_h);
     d.out = y_fold ? y_fold : (void*)ydisp;
     d.slot_token = slot_token;
@@ -379,6 +395,8 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g1.N = p.F;
   g1.K = p.H;
   g1.B = w->w1;
+  g1.Bp = w->w1_experts;
+  g1.biasp = w->b1_experts;
   g1.b_stride = (long long)p.F * p.H;
   g1.bias = w->b1;
   g1.bias_stride = p.F;
@@ -403,6 +421,8 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g2.N = p.H;
   g2.K = p.F;
   g2.B = w->w2;
+  g2.Bp = w->w2_experts;
+  g2.biasp = w->b2_experts;
   g2.b_stride = (long long)p.H * p.F;
   g2.bias = w->b2;
   g2.bias_stride = p.H;
@@ -484,6 +504,10 @@ moe_status_t check_ws(const void* ws, size_t have, size_t need) {
 }
 
 }  // namespace
+
+namespace moe {
+moe_status_t api_error(moe_status_t st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace moe
 
 // ================================================================ C ABI
 extern "C" {

@@ -198,3 +198,27 @@ def test_bench_stacks_are_chainable():
         assert len({(s.T, s.H, s.dtype) for s in shapes}) == 1, name
         for s in shapes:
             B.moe_layer_plan(B.desc_from_shape(s))
+
+
+def test_expert_tables_and_store_argument_errors():
+    """Per-expert pointer tables must come as a set of four; the expert store's
+    entry points reject bad arguments on the host (no device needed for these)."""
+    L = B.lib()
+    d = _desc()
+    need = B.moe_workspace_size(d)
+    ok = ctypes.c_void_p(0x100000)
+    w = B.LayerWeights(*([ok.value] * 10))
+    w.w1_experts = ok.value                       # one table without the other three
+    st = L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), ok, ok, ok, need, None)
+    assert st == B.MOE_ERR_INVALID_ARGUMENT and b"pointer tables" in L.moe_last_error()
+    h = ctypes.c_void_p()
+    assert L.moe_expert_store_create(None, 1, ctypes.byref(h)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_create(ctypes.byref(d), -1, ctypes.byref(h)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_create(ctypes.byref(d), d.num_local_experts + 1, ctypes.byref(h)) \
+        == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_create(ctypes.byref(d), 1, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_destroy(None) == B.MOE_OK
+    assert L.moe_expert_store_set_expert(None, 0, ok, ok, ok, ok) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_weights(None, ctypes.byref(w)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_update(None, ok, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_residency(None, ok) == B.MOE_ERR_INVALID_ARGUMENT
