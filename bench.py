@@ -88,6 +88,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode_350m_moe128", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--store-slots", type=int, default=None,
+                    help="keep the experts in pinned host memory with this many device slots (expert store)")
     ap.add_argument("--stack", default=None, choices=sorted(W.STACKS),
                     help="time a stack of MoE layers chained through their outputs instead of one layer")
     ap.add_argument("--layers", type=int, default=None, help="independent weight sets rotated per step")
@@ -120,7 +122,14 @@ def main():
     # ---- inputs, resident in HBM before any timing
     weights = [W.make_weights(shape, seed=s, device=dev) for s in range(n_layers)]
     xs = [W.make_x(shape, seed=1000 + b, device=dev) for b in range(n_batches)]
-    layers = [B.MoELayer(shape, w) for w in weights]
+    stores = []
+    if args.store_slots is not None:
+        # experts in pinned host memory, a device cache of store_slots experts per layer
+        for w in weights:
+            st_ = B.ExpertStore(shape, args.store_slots)
+            st_.fill({k: w[k].cpu() for k in ("w1", "b1", "w2", "b2")})
+            stores.append(st_)
+    layers = [B.MoELayer(shape, w, store=stores[i] if stores else None) for i, w in enumerate(weights)]
     ws = layers[0].ws
     for L in layers[1:]:
         L.ws = ws
@@ -139,6 +148,8 @@ def main():
     offsets = torch.empty(shape.E_loc + 1, dtype=torch.int32, device=dev)
     slot_token = torch.empty(max(R_max, 1), dtype=torch.int32, device=dev)
     token_slot = torch.empty((shape.T, shape.k), dtype=torch.int32, device=dev)
+    active_sets = {}
+    demand_sum = np.zeros((n_layers, shape.E), dtype=np.int64)
     for li in range(n_layers):
         for bi in range(n_batches):
             B.moe_gate(desc, xs[bi], weights[li]["gate_w"], weights[li]["gate_b"], idx, tw, None, ws)
@@ -146,6 +157,22 @@ def main():
             off = offsets.cpu().numpy()
             n_active[li, bi] = int((np.diff(off) > 0).sum())
             rows[li, bi] = int(off[-1])
+            active_sets[li, bi] = np.nonzero(np.diff(off) > 0)[0]
+            demand_sum[li] += demand.cpu().numpy()
+    store_info = None
+    if stores:
+        # residency from the demand of all batches, fixed during the timed steps
+        copied = [st_.update(np.minimum(demand_sum[li], 2**31 - 1).astype(np.int32), stream)
+                  for li, st_ in enumerate(stores)]
+        res = [st_.residency() for st_ in stores]
+        hits = [np.mean(res[li][active_sets[li, bi]] >= 0) if len(active_sets[li, bi]) else 1.0
+                for li in range(n_layers) for bi in range(n_batches)]
+        host_experts = np.mean([np.sum(res[li][active_sets[li, bi]] < 0)
+                                for li in range(n_layers) for bi in range(n_batches)])
+        store_info = {"slots": args.store_slots, "experts_copied": int(sum(copied)),
+                      "resident_hit_rate": round(float(np.mean(hits)), 4),
+                      "host_read_experts_per_step": round(float(host_experts), 3),
+                      "host_read_bytes_per_step": int(host_experts * expert_unit_bytes(shape))}
     del idx, tw, demand, offsets, slot_token, token_slot
     torch.cuda.synchronize()
 
@@ -289,6 +316,7 @@ def main():
                    "capacity_factor": shape.cf, "mlp_type": shape.mlp_type, "weight_sets": n_layers,
                    "token_batches": n_batches, "parallelism": "one GPU"},
         "roofline": roof,
+        **({"store": store_info} if store_info else {}),
         "layer": {"hbm_frac": round(lay_b / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "mfma_frac": round(lay_f / (ms_per_step / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                   "algorithmic_bytes": int(lay_b), "algorithmic_flops": int(lay_f),
@@ -299,6 +327,8 @@ def main():
     print("[bench] event passes done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, weights[0], xs, args.cpu_seconds)
+    for st_ in stores:
+        st_.close()
     print(json.dumps(out), flush=True)
 
 
