@@ -145,8 +145,11 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte load marked non-temporal: data streamed once (expert weights) should
 // not displace reused lines from the caches.
+// global address space stated so the load is a global_load, never a flat one
+// (a flat load also counts against lgkmcnt, so LDS waits would wait for it)
 __device__ inline uint4 ld_nt16(const void* ptr) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ptr));
+  typedef const __attribute__((address_space(1))) u32x4_t* gptr_t;
+  const u32x4_t v = __builtin_nontemporal_load((gptr_t)ptr);
   return __builtin_bit_cast(uint4, v);
 }
 

@@ -120,16 +120,22 @@ __device__ inline float dot_rows(const uint4 (&wv)[RPW][NQ], const typename DT::
   return wave_reduce_multi<RPW * MAXM>(acc);
 }
 
-// Route a decode-sized batch (k*T <= 64) inside one work-group, entirely in LDS.
-// Top-k per token (one wave per token; work-group 0 also computes the softmax
-// weights), then, with one thread per assignment a (rank-major a = j*T + t):
-//   pos(a)  = earlier assignments to the same expert
-//   kept(a) = local expert and pos(a) < C
-//   slot(a) = kept assignments to lower local experts + pos(a)
-// which is the dispatch written out by direct counting (O(kT) per thread, no
-// scans). The g-th non-empty local expert is the g-th lowest expert among the
-// assignments with pos = 0 that are kept. Every work-group of the first expert
-// kernel does this for itself; work-group 0 also writes the routing out.
+// Route a decode-sized batch (k*T <= 64) inside one work-group, entirely in LDS,
+// in two phases so that the work-group's weight loads go out after the first:
+//   phase 1: top-k of every token (one wave per token; work-group 0 also
+//            computes the softmax weights); the expert of this work-group's
+//            assignment a (rank-major a = j*T + t) is then known;
+//   phase 2: with one thread per assignment b,
+//            pos(b)  = earlier assignments to the same expert
+//            kept(b) = local expert and pos(b) < C
+//            slot(b) = kept assignments to lower local experts + pos(b)
+//            which is the dispatch written out by direct counting (O(kT) per
+//            thread, no scans). Assignment a leads its expert's segment when it
+//            is kept with pos 0; the segment is rows [slot(a), slot(a) + kept
+//            count of the expert). Work-group 0 also writes the routing out.
+// Work-groups of assignments that do not lead a segment (duplicates of an
+// expert, drops, non-local experts) end after phase 2; their weight loads, if
+// any, read lines the leader reads too.
 #define UP_WAVES 8
 #define ROUTE_NTH (UP_WAVES * 64)
 #define ROUTE_MAX_KT 64
@@ -137,109 +143,133 @@ __host__ __device__ inline size_t route_lds_ints(int T, int k, int R_max) {
   return 5 * (size_t)T * k + R_max + 4;
 }
 
-// Returns false if this work-group's segment g does not exist; else seg, r0, r1
-// and lst (slot -> token, in LDS).
-__device__ inline bool route_tiny_lds(const RouteParams& rp, int H, int g, int* sh, int& seg, int& r0, int& r1,
-                                      const int*& lst_out) {
+struct RouteLds {
+  int* lidx;    // [T][k] chosen experts
+  float* lw;    // [T][k] weights (work-group 0)
+  int* lkey;    // [kT] rank-major keys (E = none)
+  int* lpos;    // [kT] pos(b), or -1 when not kept
+  int* lslot;   // [kT] slot(b) or -1
+  int* lst;     // [R_max] slot -> token
+  int* sinfo;   // seg, r0, r1, total
+};
+
+__device__ inline RouteLds route_lds(const RouteParams& rp, int* sh) {
+  const int kT = rp.T * rp.k;
+  RouteLds L;
+  L.lidx = sh;
+  L.lw = reinterpret_cast<float*>(L.lidx + kT);
+  L.lkey = reinterpret_cast<int*>(L.lw + kT);
+  L.lpos = L.lkey + kT;
+  L.lslot = L.lpos + kT;
+  L.lst = L.lslot + kT;
+  L.sinfo = L.lst + rp.R_max;
+  return L;
+}
+
+// Phase 1. Returns the local expert of assignment a, or -1 (a >= kT, non-local).
+__device__ inline int route_phase1(const RouteParams& rp, const RouteLds& L, int a) {
   constexpr int NW = ROUTE_NTH / 64;
-  const int E = rp.E, T = rp.T, k = rp.k, kT = T * k;
-  int* lidx = sh;                                     // [T][k] chosen experts
-  float* lw = reinterpret_cast<float*>(lidx + kT);    // [T][k] weights (work-group 0)
-  int* lkey = reinterpret_cast<int*>(lw + kT);        // [kT] rank-major keys (E = none)
-  int* lpos = lkey + kT;                              // [kT] pos(a), or -1 when not kept
-  int* lslot = lpos + kT;                             // [kT] slot(a) or -1
-  int* lst = lslot + kT;                              // [R_max] slot -> token
-  int* sinfo = lst + rp.R_max;                        // seg, r0, r1, total
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int E = rp.E, T = rp.T, k = rp.k;
+  const int w = threadIdx.x >> 6;
   const bool writer = blockIdx.x == 0;
   for (int t = w; t < T; t += NW) {
     if (writer) {
       int sel[2];
-      wave_softmax_topk(rp.z + (long long)t * E, E, k, rp.renorm != 0, nullptr, lidx + t * k, lw + t * k, sel);
+      wave_softmax_topk(rp.z + (long long)t * E, E, k, rp.renorm != 0, nullptr, L.lidx + t * k, L.lw + t * k, sel);
     } else {
-      wave_topk_only(rp.z + (long long)t * E, E, k, lidx + t * k);
+      wave_topk_only(rp.z + (long long)t * E, E, k, L.lidx + t * k);
     }
   }
-  if (tid == 0) sinfo[0] = -1;
   __syncthreads();
+  // retire every load of the top-k here (vmcnt 0): otherwise the paths with and
+  // without weight loads merge with loads of unknown age in flight and phase 2
+  // would wait for the weight loads too
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (a >= T * k) return -1;
+  const int e = L.lidx[(a - (a / T) * T) * k + a / T];
+  return (e >= rp.e_lo && e < rp.e_lo + rp.E_loc) ? e - rp.e_lo : -1;
+}
+
+// Phase 2. Returns false unless assignment a leads a segment; then seg, r0, r1
+// and lst (slot -> token, in LDS).
+__device__ inline bool route_phase2(const RouteParams& rp, const RouteLds& L, int H, int a, int& seg, int& r0,
+                                    int& r1, const int*& lst_out) {
+  const int E = rp.E, T = rp.T, k = rp.k, kT = T * k;
+  const int tid = threadIdx.x;
+  const bool writer = blockIdx.x == 0;
+  if (tid == 0) L.sinfo[0] = -1;
   // keys in rank-major order
   int key = E;
   if (tid < kT) {
     const int j = tid / T, t = tid - (tid / T) * T;
-    const int e = lidx[t * k + j];
+    const int e = L.lidx[t * k + j];
     key = (e >= 0 && e < E) ? e : E;
-    lkey[tid] = key;
+    L.lkey[tid] = key;
   }
   __syncthreads();
   const bool local = key >= rp.e_lo && key < rp.e_lo + rp.E_loc;
   int pos = 0, cnt = 0;
   if (tid < kT) {
-    for (int a = 0; a < kT; ++a) {
-      const int ka = lkey[a];
-      pos += (a < tid) & (ka == key);
-      cnt += ka == key;
+    for (int b = 0; b < kT; ++b) {
+      const int kb = L.lkey[b];
+      pos += (b < tid) & (kb == key);
+      cnt += kb == key;
     }
-    lpos[tid] = (local && pos < rp.C) ? pos : -1;
+    L.lpos[tid] = (local && pos < rp.C) ? pos : -1;
   }
   __syncthreads();
   if (tid < kT) {
     int slot = -1;
-    if (lpos[tid] >= 0) {
-      int below = 0, rank = 0;
-      for (int a = 0; a < kT; ++a) {
-        const int ka = lkey[a];
-        const bool kept_a = lpos[a] >= 0;
-        below += kept_a & (ka < key);
-        rank += kept_a & (lpos[a] == 0) & (ka < key);
-      }
+    if (L.lpos[tid] >= 0) {
+      int below = 0;
+      for (int b = 0; b < kT; ++b) below += (L.lpos[b] >= 0) & (L.lkey[b] < key);
       slot = below + pos;
-      lst[slot] = tid - (tid / T) * T;
-      if (pos == 0 && rank == g) {               // this assignment opens segment g
-        sinfo[0] = key - rp.e_lo;
-        sinfo[1] = below;
-        sinfo[2] = below + min(cnt, rp.C);
+      L.lst[slot] = tid - (tid / T) * T;
+      if (tid == a && pos == 0) {               // this work-group's assignment leads its expert's segment
+        L.sinfo[0] = key - rp.e_lo;
+        L.sinfo[1] = below;
+        L.sinfo[2] = below + min(cnt, rp.C);
       }
     }
-    lslot[tid] = slot;
+    L.lslot[tid] = slot;
   }
   if (tid == 0) {
     int total = 0;
-    for (int a = 0; a < kT; ++a) total += lpos[a] >= 0;
-    sinfo[3] = total;
+    for (int b = 0; b < kT; ++b) total += L.lpos[b] >= 0;
+    L.sinfo[3] = total;
   }
   __syncthreads();
   if (writer) {
-    const int total = sinfo[3];
-    for (int a = tid; a < kT; a += ROUTE_NTH) {
-      const int j = a / T, t = a - (a / T) * T;
-      rp.idx[t * k + j] = lidx[t * k + j];
-      rp.w[t * k + j] = lw[t * k + j];
-      rp.token_slot[t * k + j] = lslot[a];
+    const int total = L.sinfo[3];
+    for (int b = tid; b < kT; b += ROUTE_NTH) {
+      const int j = b / T, t = b - (b / T) * T;
+      rp.idx[t * k + j] = L.lidx[t * k + j];
+      rp.w[t * k + j] = L.lw[t * k + j];
+      rp.token_slot[t * k + j] = L.lslot[b];
     }
     for (int e = tid; e < E; e += ROUTE_NTH) {
       int c = 0;
-      for (int a = 0; a < kT; ++a) c += lkey[a] == e;
+      for (int b = 0; b < kT; ++b) c += L.lkey[b] == e;
       rp.demand[e] = c;
     }
     for (int i = tid; i <= rp.E_loc; i += ROUTE_NTH) {
       int c = 0;
-      for (int a = 0; a < kT; ++a) c += (lpos[a] >= 0) & (lkey[a] < rp.e_lo + i);
+      for (int b = 0; b < kT; ++b) c += (L.lpos[b] >= 0) & (L.lkey[b] < rp.e_lo + i);
       rp.offsets[i] = c;
     }
-    for (int s2 = tid; s2 < rp.R_max; s2 += ROUTE_NTH) rp.slot_token[s2] = s2 < total ? lst[s2] : -1;
+    for (int s2 = tid; s2 < rp.R_max; s2 += ROUTE_NTH) rp.slot_token[s2] = s2 < total ? L.lst[s2] : -1;
     if (rp.y_zero) {
       for (int tt = tid; tt < T; tt += ROUTE_NTH) {
         bool any = false;
-        for (int jj = 0; jj < k; ++jj) any |= lslot[jj * T + tt] >= 0;
+        for (int jj = 0; jj < k; ++jj) any |= L.lslot[jj * T + tt] >= 0;
         if (!any) zero_dropped(rp.y_zero, rp.y_esz, tt, H);
       }
     }
   }
-  seg = sinfo[0];
-  r0 = sinfo[1];
-  r1 = sinfo[2];
-  lst_out = lst;
+  seg = L.sinfo[0];
+  r0 = L.sinfo[1];
+  r1 = L.sinfo[2];
+  lst_out = L.lst;
   return seg >= 0;
 }
 
@@ -254,21 +284,32 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p
   const int g = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - g * nchunk;
   const int* a_rows = p.a_rows;
-  int seg = 0, r0 = 0, r1 = p.M;
-  if (rp.z) {
-    extern __shared__ int route_sh[];
-    if (!route_tiny_lds(rp, p.H, g, route_sh, seg, r0, r1, a_rows)) return;
-  } else if (p.seg_off) {
-    if (!find_active(p.seg_off, p.nseg, g, seg, r0, r1)) return;
-  } else if (g > 0) {
-    return;
-  }
   const long long H = p.H, F = p.F;
   const int f0 = chunk * UP_WAVES * RPW + wave * RPW;
   uint4 wv[RPW][NQ];
-  const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[seg]) : reinterpret_cast<const T*>(p.w1) + (long long)seg * F * H;
-  load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H, H);
-  __builtin_amdgcn_sched_barrier(0);   // every weight load is in flight before anything else
+  int seg = 0, r0 = 0, r1 = p.M;
+  if (rp.z) {
+    // routed here: work-group g serves assignment g; its weight loads go out as
+    // soon as the expert of g is known, the rest of the routing runs under them
+    extern __shared__ int route_sh[];
+    const RouteLds L = route_lds(rp, route_sh);
+    const int e = route_phase1(rp, L, g);
+    if (e >= 0) {
+      const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[e]) : reinterpret_cast<const T*>(p.w1) + (long long)e * F * H;
+      load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H, H);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!route_phase2(rp, L, p.H, g, seg, r0, r1, a_rows)) return;   // leads a segment: seg == e
+  } else {
+    if (p.seg_off) {
+      if (!find_active(p.seg_off, p.nseg, g, seg, r0, r1)) return;
+    } else if (g > 0) {
+      return;
+    }
+    const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[seg]) : reinterpret_cast<const T*>(p.w1) + (long long)seg * F * H;
+    load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H, H);
+    __builtin_amdgcn_sched_barrier(0);   // every weight load is in flight before anything else
+  }
   const int M = min(r1 - r0, MAXM);
   const T* x = reinterpret_cast<const T*>(p.x);
   const T* act[MAXM];

@@ -373,7 +373,9 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
     d.slot_token = slot_token;
     d.topk_w = topk_w;
     const int gsegs = (int)std::min<int64_t>(p.E_loc, p.R_max);
-    HIP_TRY(launch_decode_up(p.dtype, p.exp_maxm, d, gsegs, s, e.up_start, e.up_stop, route),
+    // routed in the kernel: one group of work-groups per assignment (see route_phase1)
+    const int gsegs_up = route ? (int)(p.T * p.k) : gsegs;
+    HIP_TRY(launch_decode_up(p.dtype, p.exp_maxm, d, gsegs_up, s, e.up_start, e.up_stop, route),
             "expert ffn up (decode)");
     ST_TRY(record(split, s));
     HIP_TRY(launch_decode_down(p.dtype, p.exp_maxm, d, gsegs, y_fold != nullptr, s, e.down_start, e.down_stop),
