@@ -53,9 +53,12 @@ __device__ inline bool find_active(const int* __restrict__ seg_off, int nseg, in
   return false;
 }
 
+#ifndef DEC_WEIGHT_VECS
+#define DEC_WEIGHT_VECS 16   // 16-byte weight vectors each lane holds in flight
+#endif
 template <int NQ, int MAXM>
 struct DecRows {
-  static constexpr int by_regs = (16 / NQ) > 0 ? 16 / NQ : 1;
+  static constexpr int by_regs = (DEC_WEIGHT_VECS / NQ) > 0 ? DEC_WEIGHT_VECS / NQ : 1;
   static constexpr int by_red = 64 / MAXM;
   static constexpr int RPW = by_regs < by_red ? by_regs : by_red;    // weight rows per wave
 };
@@ -136,7 +139,9 @@ __device__ inline float dot_rows(const uint4 (&wv)[RPW][NQ], const typename DT::
 // Work-groups of assignments that do not lead a segment (duplicates of an
 // expert, drops, non-local experts) end after phase 2; their weight loads, if
 // any, read lines the leader reads too.
+#ifndef UP_WAVES
 #define UP_WAVES 8
+#endif
 #define ROUTE_NTH (UP_WAVES * 64)
 #define ROUTE_MAX_KT 64
 __host__ __device__ inline size_t route_lds_ints(int T, int k, int R_max) {
