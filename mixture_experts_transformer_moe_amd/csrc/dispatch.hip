@@ -14,6 +14,7 @@
 #include "kernels.h"
 #include "dispatch_common.h"
 #include "topk.h"
+#include "tile_plan.h"
 
 namespace moe {
 
@@ -39,9 +40,10 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_count_kernel(const int* _
 __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scan_kernel(int* __restrict__ blk_hist, int nblk,
                                                                    int E, int e_lo, int E_loc, int C,
                                                                    int* __restrict__ demand,
-                                                                   int* __restrict__ offsets) {
+                                                                   int* __restrict__ offsets, TilePlanArgs plan) {
   __shared__ int sdem[1024];
   __shared__ int ssc[DISP_WAVES + 1];
+  __shared__ int plds[tile_plan_lds_ints(DISP_BLOCK)];
   const int tid = threadIdx.x;
   if (tid < E) {
     int run = 0;
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scan_kernel(int* __restri
   const int off = block_excl_scan<DISP_BLOCK>(kept, ssc, &total);
   if (tid < E_loc) offsets[tid] = off;
   if (tid == 0) offsets[E_loc] = total;
+  if (plan.list1 || plan.list2) tile_plan_body<DISP_BLOCK>(kept, E_loc, plan, plds);
 }
 
 __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
@@ -95,12 +98,13 @@ template <int MODE, int NTH>
 __device__ inline void dispatch_small_body(int* sh, const float* z, int renorm, float* probs, float* topk_w, int* idx,
                                            int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                            int* demand, int* offsets, int* slot_token, int* token_slot,
-                                           void* y_zero, int y_esz, int H) {
+                                           void* y_zero, int y_esz, int H, const TilePlanArgs& plan) {
   constexpr int NW = NTH / MOE_WAVE;
   int* wcnt = sh;                                   // NW * (E + 1)
   int* tot = wcnt + NW * (E + 1);                   // E
   int* sidx = tot + E;                              // NTH
   int* ssc = sidx + NTH;                            // NW + 1
+  int* plds = ssc + NW + 1;                         // tile_plan_lds_ints(NTH)
   const int tid = threadIdx.x;
   const int kT = T * k;
   if (MODE == 1) {
@@ -144,16 +148,17 @@ __device__ inline void dispatch_small_body(int* sh, const float* z, int renorm, 
     if (y_zero && slot < 0) zero_dropped(y_zero, y_esz, t, H);
   }
   for (int s = total + tid; s < R_max; s += NTH) slot_token[s] = -1;
+  if (plan.list1 || plan.list2) tile_plan_body<NTH>(kept, E_loc, plan, plds);
 }
 
 template <int MODE, int NTH>
 __global__ __launch_bounds__(NTH) void dispatch_small_kernel(
     const float* z, int renorm, float* probs, float* __restrict__ topk_w, int* idx, int T, int k, int E,
     int e_lo, int E_loc, int C, int R_max, int* __restrict__ demand, int* __restrict__ offsets,
-    int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H) {
+    int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H, TilePlanArgs plan) {
   extern __shared__ int sh[];
   dispatch_small_body<MODE, NTH>(sh, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets,
-                                 slot_token, token_slot, y_zero, y_esz, H);
+                                 slot_token, token_slot, y_zero, y_esz, H, plan);
 }
 
 // Gather x rows into the dispatched order (zero rows past the last one).
@@ -176,34 +181,41 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const typename DT::T* 
 // -------------------------------------------------------------------- launchers
 template <int NTH>
 static size_t small_lds(int E) {
-  return sizeof(int) * ((size_t)(NTH / MOE_WAVE) * (E + 1) + E + NTH + NTH / MOE_WAVE + 1);
+  return sizeof(int) * ((size_t)(NTH / MOE_WAVE) * (E + 1) + E + NTH + NTH / MOE_WAVE + 1 + tile_plan_lds_ints(NTH));
+}
+static TilePlanArgs plan_or_none(const TilePlanArgs* plan) {
+  TilePlanArgs none{};
+  return plan ? *plan : none;
 }
 size_t dispatch_small_lds(int E) { return small_lds<DISP_BLOCK>(E); }
 
 template <int NTH>
 static void launch_small_t(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w, int* idx, int T,
                            int k, int E, int e_lo, int E_loc, int C, int R_max, int* demand, int* offsets,
-                           int* slot_token, int* token_slot, void* y_zero, int y_esz, int H, hipStream_t s) {
+                           int* slot_token, int* token_slot, void* y_zero, int y_esz, int H,
+                           const TilePlanArgs& plan, hipStream_t s) {
   const size_t lds = small_lds<NTH>(E);
   if (fuse_topk)
     hipLaunchKernelGGL((dispatch_small_kernel<1, NTH>), dim3(1), dim3(NTH), lds, s, z, renorm, probs, topk_w, idx, T,
-                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H);
+                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H, plan);
   else
     hipLaunchKernelGGL((dispatch_small_kernel<0, NTH>), dim3(1), dim3(NTH), lds, s, z, renorm, probs, topk_w, idx, T,
-                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H);
+                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H, plan);
 }
 
 // One block of 256 threads when the assignments and local experts fit, else 1024.
 hipError_t launch_dispatch_small(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w,
                                  int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* demand, int* offsets, int* slot_token, int* token_slot, void* y_zero,
-                                 int y_esz, int H, hipStream_t s) {
+                                 int y_esz, int H, const TilePlanArgs* plan, hipStream_t s) {
+  if (T * k > DISP_BLOCK || E_loc > DISP_BLOCK) return hipErrorInvalidValue;
+  const TilePlanArgs pl = plan_or_none(plan);
   if (T * k <= 256 && E_loc <= 256)
     launch_small_t<256>(fuse_topk, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets,
-                        slot_token, token_slot, y_zero, y_esz, H, s);
+                        slot_token, token_slot, y_zero, y_esz, H, pl, s);
   else
     launch_small_t<DISP_BLOCK>(fuse_topk, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand,
-                               offsets, slot_token, token_slot, y_zero, y_esz, H, s);
+                               offsets, slot_token, token_slot, y_zero, y_esz, H, pl, s);
   return hipGetLastError();
 }
 
@@ -212,7 +224,8 @@ int dispatch_block_size() { return DISP_BLOCK; }
 
 hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* rank, int* blk_hist, int* demand, int* offsets, int* slot_token,
-                                 int* token_slot, void* y_zero, int y_esz, int H, hipStream_t s) {
+                                 int* token_slot, void* y_zero, int y_esz, int H, const TilePlanArgs* plan,
+                                 hipStream_t s) {
   const int nblk = dispatch_num_blocks((long long)T * k);
   const size_t lds = sizeof(int) * ((size_t)DISP_WAVES * (E + 1) + E);
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(DISP_BLOCK), lds, s, idx, T, k, E, rank,
@@ -220,7 +233,7 @@ hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(DISP_BLOCK), 0, s, blk_hist, nblk, E, e_lo, E_loc,
-                     C, demand, offsets);
+                     C, demand, offsets, plan_or_none(plan));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(DISP_BLOCK), 0, s, idx, rank, blk_hist, T, k,

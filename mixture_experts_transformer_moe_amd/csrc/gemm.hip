@@ -29,6 +29,7 @@
 // the 8 XCDs) and share its L2.
 #include "common.h"
 #include "kernels.h"
+#include "tile_plan.h"
 
 namespace moe {
 
@@ -339,68 +340,18 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 }
 
 // ---------------------------------------------------------------- plan kernel
-// Tile lists of the two expert GEMMs. An extra segment with mt_extra row tiles
-// (id nseg, e.g. the residual layer's dense MLP over all tokens) goes first, so
-// its tiles run alongside the expert tiles rather than after them.
-__global__ __launch_bounds__(1024) void gemm_plan_kernel(const int* __restrict__ seg_off, int nseg, int BM,
-                                                        int n_nt1, int n_nt2, int2* __restrict__ list1,
-                                                        int2* __restrict__ list2, int* __restrict__ count,
-                                                        int mt_extra) {
-  __shared__ int P[1025];
-  __shared__ int C[1024];
-  __shared__ int wsum[17];
+// Tile lists of the two expert GEMMs from the segment offsets (one block; the
+// layer forward builds them inside its dispatch kernel instead).
+__global__ __launch_bounds__(1024) void gemm_plan_kernel(const int* __restrict__ seg_off, int nseg, TilePlanArgs a) {
+  __shared__ int lds[tile_plan_lds_ints(1024)];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int c = (tid < nseg) ? (seg_off[tid + 1] - seg_off[tid] + BM - 1) / BM : 0;
-  C[tid] = c;
-  int incl = c;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < 16; ++i) { const int t = wsum[i]; wsum[i] = run; run += t; }
-    wsum[16] = run;
-  }
-  __syncthreads();
-  P[tid] = wsum[w] + incl - c;
-  if (tid == 0) P[nseg] = wsum[16];
-  __syncthreads();
-  const int total = wsum[16];
-  if (tid == 0) count[0] = total + mt_extra;
-  for (int g = 0; g < 2; ++g) {
-    const int n_nt = g ? n_nt2 : n_nt1;
-    int2* list = g ? list2 : list1;
-    if (!list) continue;
-    const int n_extra = mt_extra * n_nt;
-    for (int L = tid; L < n_extra; L += 1024) {
-      const int nt = L / mt_extra, mt = L - nt * mt_extra;
-      list[L] = make_int2(nseg, (nt << 16) | mt);
-    }
-    for (int L = tid; L < total * n_nt; L += 1024) {
-      const int v = L / n_nt;
-      int lo = 0, hi = nseg;               // largest s with P[s] <= v and P[s+1] > v
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (P[mid] <= v) lo = mid; else hi = mid;
-      }
-      const int s = lo;
-      const int q = L - P[s] * n_nt;
-      const int cs = C[s];
-      const int nt = q / cs, mt = q - (q / cs) * cs;
-      list[n_extra + L] = make_int2(s, (nt << 16) | mt);
-    }
-  }
+  const int rows = (tid < nseg) ? seg_off[tid + 1] - seg_off[tid] : 0;
+  tile_plan_body<1024>(rows, nseg, a, lds);
 }
 
-hipError_t launch_gemm_plan(const int* seg_off, int nseg, int BM, int n_nt1, int n_nt2, int2* list1, int2* list2,
-                            int* count, hipStream_t s, int mt_extra) {
-  hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, seg_off, nseg, BM, n_nt1, n_nt2, list1, list2,
-                     count, mt_extra);
+hipError_t launch_gemm_plan(const int* seg_off, int nseg, const TilePlanArgs& a, hipStream_t s) {
+  if (nseg > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, seg_off, nseg, a);
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 #include <stddef.h>
 
 #include "common.h"
+#include "tile_plan.h"
 
 namespace moe {
 
@@ -19,23 +20,22 @@ size_t dispatch_small_lds(int E);
 int dispatch_num_blocks(long long kT);
 int dispatch_block_size();
 // y_zero (nullable): output rows of tokens with no kept assignment are zeroed there.
+// plan (nullable): the expert GEMMs' tile lists are built from the kept rows too.
 hipError_t launch_dispatch_small(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w,
                                  int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* demand, int* offsets, int* slot_token, int* token_slot, void* y_zero,
-                                 int y_esz, int H, hipStream_t s);
+                                 int y_esz, int H, const TilePlanArgs* plan, hipStream_t s);
 hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* rank, int* blk_hist, int* demand, int* offsets, int* slot_token,
-                                 int* token_slot, void* y_zero, int y_esz, int H, hipStream_t s);
+                                 int* token_slot, void* y_zero, int y_esz, int H, const TilePlanArgs* plan,
+                                 hipStream_t s);
 hipError_t launch_gather_rows(int dtype, const void* x, const int* slot_token, int R_max, int H, void* xd,
                               hipStream_t s);
 
 // gemm.hip
 enum { EPI_GELU = 0, EPI_F32 = 1 };
-// Tile list for segments [seg_off[s], seg_off[s+1]) with BM-row m-tiles, for two
-// GEMMs with n_nt1 / n_nt2 column tiles, preceded by mt_extra m-tiles of the
-// extra segment (id nseg, see GemmParams). count[0] = number of m-tiles.
-hipError_t launch_gemm_plan(const int* seg_off, int nseg, int BM, int n_nt1, int n_nt2, int2* list1,
-                            int2* list2, int* count, hipStream_t s, int mt_extra = 0);
+// Tile lists for segments [seg_off[s], seg_off[s+1]) (nseg <= 1024), see TilePlanArgs.
+hipError_t launch_gemm_plan(const int* seg_off, int nseg, const TilePlanArgs& a, hipStream_t s);
 // bias_f32 selects a float bias (gate) instead of a dtype bias.
 // ev0 / ev1 (nullable): recorded by the kernel dispatch itself (start / end).
 hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN, const GemmParams& p,

@@ -320,24 +320,40 @@ moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, c
   return MOE_OK;
 }
 
+// plan (nullable): the dispatch kernel that computes the segment offsets also
+// writes the expert GEMMs' tile lists.
 moe_status_t run_dispatch(const Plan& p, bool fuse_topk, const float* z, float* probs, float* topk_w, int* idx,
                           int* demand, int* offsets, int* slot_token, int* token_slot, void* y_zero, void* ws,
-                          hipStream_t s) {
+                          hipStream_t s, const TilePlanArgs* plan = nullptr) {
   const int C = (int)std::min<int64_t>(p.C, INT32_MAX);
   if (p.disp_small) {
     HIP_TRY(launch_dispatch_small(fuse_topk, z, p.renorm ? 1 : 0, probs, topk_w, idx, (int)p.T, p.k, p.E, p.e_lo,
                                   p.E_loc, C, (int)p.R_max, demand, offsets, slot_token, token_slot, y_zero,
-                                  (int)p.esz, p.H, s),
+                                  (int)p.esz, p.H, plan, s),
             "dispatch (one block)");
-  } else {
-    if (fuse_topk)
-      HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, idx, topk_w, probs, s), "softmax/top-k");
-    HIP_TRY(launch_dispatch_multi(idx, (int)p.T, p.k, p.E, p.e_lo, p.E_loc, C, (int)p.R_max, wsp<int>(ws, p.o_rank),
-                                  wsp<int>(ws, p.o_blk), demand, offsets, slot_token, token_slot, y_zero,
-                                  (int)p.esz, p.H, s),
-            "dispatch");
+    return MOE_OK;
   }
+  if (fuse_topk)
+    HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, idx, topk_w, probs, s), "softmax/top-k");
+  HIP_TRY(launch_dispatch_multi(idx, (int)p.T, p.k, p.E, p.e_lo, p.E_loc, C, (int)p.R_max, wsp<int>(ws, p.o_rank),
+                                wsp<int>(ws, p.o_blk), demand, offsets, slot_token, token_slot, y_zero,
+                                (int)p.esz, p.H, plan, s),
+          "dispatch");
   return MOE_OK;
+}
+
+// The expert GEMMs' tile lists in the workspace (with the extra segment's row
+// tiles when the dense MLP runs inside the expert GEMMs).
+TilePlanArgs tile_plan_args(const Plan& p, void* ws, bool with_dense) {
+  TilePlanArgs a{};
+  a.list1 = wsp<int2>(ws, p.o_list1);
+  a.list2 = wsp<int2>(ws, p.o_list2);
+  a.count = wsp<int>(ws, p.o_count);
+  a.BM = p.BM;
+  a.n_nt1 = p.F / p.BN1;
+  a.n_nt2 = p.H / p.BN2;
+  a.mt_extra = (with_dense && p.dense_in_experts) ? p.mt_extra : 0;
+  return a;
 }
 
 // Expert FFN. x rows come from x via slot_token (a_rows != null) or from
@@ -348,7 +364,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
                          const moe_layer_weights_t* w, float* ydisp, void* ws, hipStream_t s,
                          void* y_fold = nullptr, const int* slot_token = nullptr, const float* topk_w = nullptr,
                          const moe_phase_events_t* ev = nullptr, const RouteParams* route = nullptr,
-                         bool with_dense = false) {
+                         bool with_dense = false, bool plan_ready = false) {
   const moe_phase_events_t none{};
   const moe_phase_events_t& e = ev ? *ev : none;
   hipEvent_t split = e.ffn_split;
@@ -387,7 +403,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   int* cnt = wsp<int>(ws, p.o_count);
   const int nt1 = p.F / p.BN1, nt2 = p.H / p.BN2;
   const bool dense = with_dense && p.dense_in_experts;
-  HIP_TRY(launch_gemm_plan(offsets, p.E_loc, p.BM, nt1, nt2, l1, l2, cnt, s, dense ? p.mt_extra : 0), "gemm plan");
+  if (!plan_ready) HIP_TRY(launch_gemm_plan(offsets, p.E_loc, tile_plan_args(p, ws, with_dense), s), "gemm plan");
   void* h = wsp<void>(ws, p.o_h);
   GemmParams g1{};
   g1.A = x;
@@ -548,8 +564,11 @@ moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out) {
   out->tile_rows = p.exp_decode ? 0 : p.BM;
   out->tile_cols_w1 = p.exp_decode ? 0 : p.BN1;
   out->tile_cols_w2 = p.exp_decode ? 0 : p.BN2;
-  out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) +
-                  (p.exp_decode ? 2 : 3) + ((p.residual && !p.dense_in_experts) ? 2 : 0) + (p.fold_combine ? 0 : 1);
+  // gate; dispatch (one block, or softmax/top-k + count, scan, scatter); two
+  // expert kernels (the GEMMs' tile lists come from the dispatch); the dense
+  // MLP's two unless inside the expert GEMMs; combine
+  out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) + 2 +
+                  ((p.residual && !p.dense_in_experts) ? 2 : 0) + (p.fold_combine ? 0 : 1);
   return MOE_OK;
 }
 
@@ -691,14 +710,17 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
     rp.y_zero = y_fold;
     rp.y_esz = (int)p.esz;
   } else {
-    ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot, y_fold, ws, stream));
+    // the GEMM path's tile lists come out of the dispatch kernel that finds the offsets
+    const TilePlanArgs tp = tile_plan_args(p, ws, true);
+    ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot, y_fold, ws, stream,
+                        p.exp_decode ? nullptr : &tp));
   }
   ST_TRY(record(e.dispatch_end, stream));
   ST_TRY(record(e.ffn_begin, stream));
   float* ydisp = wsp<float>(ws, p.o_ydisp);
   if (p.R_max > 0 || p.dense_in_experts)
     ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream, y_fold, slot_token, tw, ev,
-                       p.route_in_up ? &rp : nullptr, true));
+                       p.route_in_up ? &rp : nullptr, true, true));
   float* dense = nullptr;
   if (p.residual) {
     dense = wsp<float>(ws, p.o_dense);

@@ -93,15 +93,15 @@ BAD = [
 def test_layer_plan_paths():
     """The plan names the path each benchmark layer takes and agrees with the
     sizing calls."""
-    # launches: gate logits; softmax/top-k + count, scan, scatter (or none when
-    # the first expert kernel routes); the expert kernels (tile plan + two GEMMs,
-    # or two streaming kernels); the dense MLP's two (none when its tiles join the
-    # expert GEMMs); the combine unless folded
+    # launches: gate logits; the dispatch (none when the first expert kernel
+    # routes; else softmax/top-k + count, scan, scatter), whose single-block
+    # kernel also writes the GEMM tile lists; the two expert kernels; the dense
+    # MLP's two (none when its tiles join the expert GEMMs); the combine unless folded
     expect = {  # name: (gate, experts, dispatch in expert kernel, combine in expert kernel, launches)
         "decode_350m_moe128": ("vector", "stream", True, True, 1 + 0 + 2 + 0),
-        "prefill_1p3b_moe128": ("matrix", "grouped_gemm", False, False, 1 + 4 + 3 + 1),
-        "prmoe_residual": ("matrix", "grouped_gemm", False, False, 1 + 4 + 3 + 0 + 1),   # MLP inside the GEMMs
-        "share_24b_moe128": ("matrix", "grouped_gemm", False, False, 1 + 4 + 3 + 1),
+        "prefill_1p3b_moe128": ("matrix", "grouped_gemm", False, False, 1 + 4 + 2 + 1),
+        "prmoe_residual": ("matrix", "grouped_gemm", False, False, 1 + 4 + 2 + 0 + 1),   # MLP inside the GEMMs
+        "share_24b_moe128": ("matrix", "grouped_gemm", False, False, 1 + 4 + 2 + 1),
     }
     for name, (gate, experts, disp, comb, launches) in expect.items():
         shape = W.WORKLOADS[name]

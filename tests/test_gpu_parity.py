@@ -58,6 +58,10 @@ CASES = {
     "share_eloc1": W.LayerShape("el1", T=256, H=256, F=512, E=16, E_loc=1, e_lo=5, k=2, cf=1.0, dtype="bf16"),
     # streaming expert kernels fed by the dispatch kernel (batch too large to route in-kernel)
     "decode_unrouted": W.LayerShape("decun", T=512, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
+    # the multi-block dispatch writing the GEMM tile lists from its scan block:
+    # sixteen dispatch blocks with one expert, and eighteen with 32 experts, top-2
+    "gemm_multi_e8": W.LayerShape("gm8", T=16384, H=64, F=128, E=8, E_loc=8, k=1, cf=1.0, dtype="f16"),
+    "gemm_multi_block": W.LayerShape("gmb", T=9000, H=128, F=256, E=32, E_loc=32, k=2, cf=1.0, dtype="f16"),
 }
 
 
@@ -120,6 +124,9 @@ def test_steps_and_layer_match_oracle(name):
     (777, 5, 2, 3, 1, 0.5, False),
     (1024, 8, 1, 8, 0, 1.0, True),        # exactly one block
     (1025, 8, 1, 8, 0, 1.0, True),        # one block plus one assignment
+    (5000, 512, 2, 512, 0, 1.0, False),   # multi-block with the largest expert count
+    (16385, 8, 1, 8, 0, 1.0, True),       # seventeen blocks, the last holding one assignment
+    (9000, 32, 2, 24, 4, 1.0, False),     # multi-block, local share, top-2
 ])
 def test_dispatch_fed_oracle_routing(T, E, k, E_loc, e_lo, cf, hot):
     G.say(f"[dispatch] T={T} E={E} k={k} E_loc={E_loc} e_lo={e_lo} cf={cf} hot={hot}")
