@@ -190,6 +190,10 @@ struct GemmParams {
   const void* bias2;
   void* C2;
   int M2;
+  // split over K (fp32 output, float bias): grid.y = ksplit slices of K, slice s
+  // writes its partial sums to C + s * c_split (bias in slice 0 only); 0 or 1: none
+  int ksplit;
+  long long c_split;
 };
 
 // Expert FFN for segments of at most MAXM rows: each work-group takes one

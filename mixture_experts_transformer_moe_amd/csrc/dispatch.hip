@@ -98,7 +98,7 @@ template <int MODE, int NTH>
 __device__ inline void dispatch_small_body(int* sh, const float* z, int renorm, float* probs, float* topk_w, int* idx,
                                            int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                            int* demand, int* offsets, int* slot_token, int* token_slot,
-                                           void* y_zero, int y_esz, int H, const TilePlanArgs& plan) {
+                                           void* y_zero, int y_esz, int H, const TilePlanArgs& plan, int zsplit) {
   constexpr int NW = NTH / MOE_WAVE;
   int* wcnt = sh;                                   // NW * (E + 1)
   int* tot = wcnt + NW * (E + 1);                   // E
@@ -112,7 +112,7 @@ __device__ inline void dispatch_small_body(int* sh, const float* z, int renorm, 
     for (int t = w; t < T; t += NW) {
       int sel[2];
       wave_softmax_topk(z + (long long)t * E, E, k, renorm != 0, probs ? probs + (long long)t * E : nullptr,
-                        idx + (long long)t * k, topk_w + (long long)t * k, sel);
+                        idx + (long long)t * k, topk_w + (long long)t * k, sel, zsplit, (long long)T * E);
       if (lane_id() == 0)
         for (int j = 0; j < k; ++j) sidx[j * T + t] = sel[j];
     }
@@ -155,10 +155,11 @@ template <int MODE, int NTH>
 __global__ __launch_bounds__(NTH) void dispatch_small_kernel(
     const float* z, int renorm, float* probs, float* __restrict__ topk_w, int* idx, int T, int k, int E,
     int e_lo, int E_loc, int C, int R_max, int* __restrict__ demand, int* __restrict__ offsets,
-    int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H, TilePlanArgs plan) {
+    int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H, TilePlanArgs plan,
+    int zsplit) {
   extern __shared__ int sh[];
   dispatch_small_body<MODE, NTH>(sh, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets,
-                                 slot_token, token_slot, y_zero, y_esz, H, plan);
+                                 slot_token, token_slot, y_zero, y_esz, H, plan, zsplit);
 }
 
 // Gather x rows into the dispatched order (zero rows past the last one).
@@ -193,29 +194,32 @@ template <int NTH>
 static void launch_small_t(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w, int* idx, int T,
                            int k, int E, int e_lo, int E_loc, int C, int R_max, int* demand, int* offsets,
                            int* slot_token, int* token_slot, void* y_zero, int y_esz, int H,
-                           const TilePlanArgs& plan, hipStream_t s) {
+                           const TilePlanArgs& plan, int zsplit, hipStream_t s) {
   const size_t lds = small_lds<NTH>(E);
   if (fuse_topk)
     hipLaunchKernelGGL((dispatch_small_kernel<1, NTH>), dim3(1), dim3(NTH), lds, s, z, renorm, probs, topk_w, idx, T,
-                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H, plan);
+                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H, plan,
+                       zsplit);
   else
     hipLaunchKernelGGL((dispatch_small_kernel<0, NTH>), dim3(1), dim3(NTH), lds, s, z, renorm, probs, topk_w, idx, T,
-                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H, plan);
+                       k, E, e_lo, E_loc, C, R_max, demand, offsets, slot_token, token_slot, y_zero, y_esz, H, plan,
+                       zsplit);
 }
 
 // One block of 256 threads when the assignments and local experts fit, else 1024.
 hipError_t launch_dispatch_small(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w,
                                  int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* demand, int* offsets, int* slot_token, int* token_slot, void* y_zero,
-                                 int y_esz, int H, const TilePlanArgs* plan, hipStream_t s) {
+                                 int y_esz, int H, const TilePlanArgs* plan, int zsplit, hipStream_t s) {
   if (T * k > DISP_BLOCK || E_loc > DISP_BLOCK) return hipErrorInvalidValue;
   const TilePlanArgs pl = plan_or_none(plan);
+  if (zsplit < 1) zsplit = 1;
   if (T * k <= 256 && E_loc <= 256)
     launch_small_t<256>(fuse_topk, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand, offsets,
-                        slot_token, token_slot, y_zero, y_esz, H, pl, s);
+                        slot_token, token_slot, y_zero, y_esz, H, pl, zsplit, s);
   else
     launch_small_t<DISP_BLOCK>(fuse_topk, z, renorm, probs, topk_w, idx, T, k, E, e_lo, E_loc, C, R_max, demand,
-                               offsets, slot_token, token_slot, y_zero, y_esz, H, pl, s);
+                               offsets, slot_token, token_slot, y_zero, y_esz, H, pl, zsplit, s);
   return hipGetLastError();
 }
 

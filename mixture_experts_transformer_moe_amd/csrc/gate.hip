@@ -61,12 +61,12 @@ __global__ __launch_bounds__(64) void gate_logits_fma_kernel(
 __global__ __launch_bounds__(256) void softmax_topk_kernel(const float* z, int T, int E,
                                                            int k, int renorm, int* __restrict__ idx,
                                                            float* __restrict__ w,
-                                                           float* probs) {
+                                                           float* probs, int zsplit) {
   const int t = blockIdx.x * 4 + threadIdx.x / MOE_WAVE;
   if (t >= T) return;
   int sel[2];
   wave_softmax_topk(z + (long long)t * E, E, k, renorm != 0, probs ? probs + (long long)t * E : nullptr,
-                    idx + (long long)t * k, w + (long long)t * k, sel);
+                    idx + (long long)t * k, w + (long long)t * k, sel, zsplit, (long long)T * E);
 }
 
 template <typename DT, int EB>
@@ -120,9 +120,9 @@ hipError_t launch_gate_logits_fma(int dtype, const void* x, const void* wg, cons
 }
 
 hipError_t launch_softmax_topk(const float* z, int T, int E, int k, int renorm, int* idx, float* w,
-                               float* probs, hipStream_t s) {
+                               float* probs, hipStream_t s, int zsplit) {
   hipLaunchKernelGGL(softmax_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, z, T, E, k, renorm, idx,
-                     w, probs);
+                     w, probs, zsplit < 1 ? 1 : zsplit);
   return hipGetLastError();
 }
 

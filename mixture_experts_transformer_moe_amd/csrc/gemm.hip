@@ -27,6 +27,8 @@
 // the m-tiles that share a weight tile are adjacent; the block index is remapped
 // so adjacent tiles land on the same XCD (work-groups are dealt round-robin over
 // the 8 XCDs) and share its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "tile_plan.h"
@@ -231,7 +233,17 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (int)(((long long)p.K * sizeof(T)) / 128);
+  int nk = (int)(((long long)p.K * sizeof(T)) / 128);
+  if constexpr (std::is_same<BiasT, float>::value) {
+    if (p.ksplit > 1) {   // this work-group's slice of K (the host makes nk divisible)
+      nk /= p.ksplit;
+      const long long k0 = (long long)blockIdx.y * nk * 128;
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) a_src[i] += k0;
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) b_src[i] += k0;
+    }
+  }
   const int frag_row = lane & 15;
   // 16-byte column of the lane's fragment in k-block kb (0 or 1), swizzled for its row
   const int frag_c0 = (((lane >> 4)) ^ (frag_row & 7)) * 16;
@@ -336,6 +348,15 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #undef GEMM_MATH
 #undef GEMM_SB
 
+  if constexpr (std::is_same<BiasT, float>::value) {
+    if (p.ksplit > 1) {   // partial sums of this slice; the bias goes with slice 0
+      GemmParams q = p;
+      q.C = reinterpret_cast<float*>(p.C) + (long long)blockIdx.y * p.c_split;
+      if (blockIdx.y != 0) q.bias = nullptr;
+      gemm_epilogue<DT, EPI, BiasT, TN, TM>(q, acc, seg, nt * BN + wave_n * TN * 16, m0 + wave_m * TM * 16, r1, lane);
+      return;
+    }
+  }
   gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + wave_m * TM * 16, r1, lane);
 }
 
@@ -367,8 +388,8 @@ template <typename DT, int BM, int BN, int EPI, typename BiasT>
 static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   constexpr int NTH = BN == 256 ? 512 : GEMM_THREADS;
   constexpr int DEPTH = (BM <= 64 || (NTH == 512 && BM == 128)) ? 2 : 1;
-  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH>), dim3(grid), dim3(NTH), 0, s, ev.start,
-             ev.stop, p);
+  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH>), dim3(grid, p.ksplit > 1 ? p.ksplit : 1),
+             dim3(NTH), 0, s, ev.start, ev.stop, p);
 }
 
 template <typename DT, int BM, int BN>
@@ -414,6 +435,11 @@ static bool launch_bn(int BM, int BN, int epi, bool bias_f32, const GemmParams& 
 hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN, const GemmParams& p, int grid,
                                hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (grid <= 0) return hipSuccess;
+  if (p.ksplit > 1) {   // fp32 partial outputs with a float bias only, and whole 128-byte steps per slice
+    const long long steps = (long long)p.K * (dtype == DT_F32 ? 4 : 2) / 128;
+    if (!bias_f32 || epi != EPI_F32 || p.tiles || steps % p.ksplit != 0 || p.ksplit > 65535)
+      return hipErrorInvalidValue;
+  }
   bool ok;
   const LaunchEv ev{ev0, ev1};
   switch (dtype) {

@@ -12,8 +12,9 @@ namespace moe {
 // gate.hip
 hipError_t launch_gate_logits_fma(int dtype, const void* x, const void* wg, const float* bias, float* z,
                                   int T, int H, int E, hipStream_t s);
+// zsplit > 1: z holds that many partial logit sums, T * E floats apart (see GemmParams::ksplit)
 hipError_t launch_softmax_topk(const float* z, int T, int E, int k, int renorm, int* idx, float* w,
-                               float* probs, hipStream_t s);
+                               float* probs, hipStream_t s, int zsplit = 1);
 
 // dispatch.hip
 size_t dispatch_small_lds(int E);
@@ -24,7 +25,7 @@ int dispatch_block_size();
 hipError_t launch_dispatch_small(bool fuse_topk, const float* z, int renorm, float* probs, float* topk_w,
                                  int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* demand, int* offsets, int* slot_token, int* token_slot, void* y_zero,
-                                 int y_esz, int H, const TilePlanArgs* plan, hipStream_t s);
+                                 int y_esz, int H, const TilePlanArgs* plan, int zsplit, hipStream_t s);
 hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, int E_loc, int C, int R_max,
                                  int* rank, int* blk_hist, int* demand, int* offsets, int* slot_token,
                                  int* token_slot, void* y_zero, int y_esz, int H, const TilePlanArgs* plan,

@@ -95,6 +95,7 @@ struct Plan {
   // gate
   bool gate_mfma;
   int gate_BM, gate_BN;
+  int gate_ksplit;     // matrix-core gate: slices of K, each writing fp32 partial logits
   // dispatch
   bool disp_small;
   int nblk;
@@ -166,18 +167,38 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   p.nblk = dispatch_num_blocks(kT);
   // gate: matrix cores when the batch fills tiles; else 4x8 wave blocks on the ALUs
   p.gate_mfma = p.T >= 64 && (p.E % 64) == 0;
-  // 64 experts per column tile and the tallest row tile that still gives every
-  // CU two work-groups: the gate streams x once and is bound by that read
-  p.gate_BN = 64;
-  p.gate_BM = 16;
-  for (int bm : {64, 32})
-    if (((p.T + bm - 1) / bm) * (p.E / 64) >= 512) { p.gate_BM = bm; break; }
   // experts: streaming kernels for tiny segments, grouped MFMA GEMM otherwise
   const int64_t seg_rows = std::min<int64_t>(p.C, kT);
   p.exp_maxm = pow2_at_least(std::max<int64_t>(seg_rows, 1));
   p.exp_decode = seg_rows <= 8 && decode_supported(p.dtype, p.H, p.F);
   p.fold_combine = p.exp_decode && p.k == 1 && !p.residual;
   p.route_in_up = p.exp_decode && route_in_decode_supported((int)p.T, p.k, p.E, p.E_loc);
+  // matrix-core gate: each K step of a work-group waits on its loads, so a
+  // short tile over all of K is latency-bound. Column tiles of 128 experts (x
+  // read once per token tile); the tallest row tile and the fewest slices of K
+  // (at least 8 steps each) that give 512 work-groups. Slices leave fp32 partial
+  // logits that the softmax / top-k adds in a fixed order. The routing inside
+  // the first decode expert kernel reads plain logits: no slices there.
+  p.gate_BN = (p.E % 128 == 0) ? 128 : 64;
+  p.gate_BM = 16;
+  p.gate_ksplit = 1;
+  if (p.gate_mfma) {
+    const int64_t steps = (int64_t)p.H * p.esz / 128;
+    bool found = false;
+    for (int bm : {64, 32, 16}) {
+      const int64_t tiles = ((p.T + bm - 1) / bm) * (p.E / p.gate_BN);
+      for (int s : {1, 2, 4, 8}) {
+        if (s > 1 && (p.route_in_up || steps % s != 0 || steps / s < 8)) break;
+        if (tiles * s >= 512) { p.gate_BM = bm; p.gate_ksplit = s; found = true; break; }
+      }
+      if (found) break;
+    }
+    if (!found) {   // small batch: the most slices allowed
+      p.gate_BM = 16;
+      for (int s : {2, 4, 8})
+        if (!p.route_in_up && steps % s == 0 && steps / s >= 8) p.gate_ksplit = s;
+    }
+  }
   p.BM = gemm_bm_for_rows(seg_rows);
   p.BN1 = (p.F % 128 == 0) ? 128 : 64;
   p.BN2 = (p.H % 128 == 0) ? 128 : 64;
@@ -228,7 +249,7 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
     return at;
   };
   const size_t T = (size_t)p.T, H = (size_t)p.H, F = (size_t)p.F, R = (size_t)p.R_max;
-  p.o_z = take(T * p.E * 4);
+  p.o_z = take(T * p.E * 4 * (size_t)p.gate_ksplit);
   p.o_idx = take(T * p.k * 4);
   p.o_w = take(T * p.k * 4);
   p.o_rank = take(p.disp_small ? 0 : T * p.k * 4);
@@ -312,6 +333,8 @@ moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, c
     g.bias = gate_b;
     g.C = z;
     g.n_ntiles = p.E / p.gate_BN;
+    g.ksplit = p.gate_ksplit;
+    g.c_split = (long long)p.T * p.E;
     const int grid = (int)((p.T + p.gate_BM - 1) / p.gate_BM) * g.n_ntiles;
     HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, true, p.gate_BM, p.gate_BN, g, grid, s), "gate logits (mfma)");
   } else {
@@ -329,12 +352,13 @@ moe_status_t run_dispatch(const Plan& p, bool fuse_topk, const float* z, float* 
   if (p.disp_small) {
     HIP_TRY(launch_dispatch_small(fuse_topk, z, p.renorm ? 1 : 0, probs, topk_w, idx, (int)p.T, p.k, p.E, p.e_lo,
                                   p.E_loc, C, (int)p.R_max, demand, offsets, slot_token, token_slot, y_zero,
-                                  (int)p.esz, p.H, plan, s),
+                                  (int)p.esz, p.H, plan, p.gate_ksplit, s),
             "dispatch (one block)");
     return MOE_OK;
   }
   if (fuse_topk)
-    HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, idx, topk_w, probs, s), "softmax/top-k");
+    HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, idx, topk_w, probs, s, p.gate_ksplit),
+            "softmax/top-k");
   HIP_TRY(launch_dispatch_multi(idx, (int)p.T, p.k, p.E, p.e_lo, p.E_loc, C, (int)p.R_max, wsp<int>(ws, p.o_rank),
                                 wsp<int>(ws, p.o_blk), demand, offsets, slot_token, token_slot, y_zero,
                                 (int)p.esz, p.H, plan, s),
@@ -583,10 +607,11 @@ moe_status_t moe_gate(const moe_layer_desc_t* d, const void* x, const void* gate
   PTR_TRY(topk_w, "topk_w");
   if (gate_b && !aligned16(gate_b)) return fail(MOE_ERR_INVALID_ARGUMENT, "gate_b is not 16-byte aligned");
   if (probs && !aligned16(probs)) return fail(MOE_ERR_INVALID_ARGUMENT, "probs is not 16-byte aligned");
-  ST_TRY(check_ws(ws, ws_bytes, align_up(p.T * p.E * 4)));
+  ST_TRY(check_ws(ws, ws_bytes, align_up(p.T * p.E * 4 * (size_t)p.gate_ksplit)));
   float* z = wsp<float>(ws, 0);
   ST_TRY(run_gate_logits(p, x, gate_w, gate_b, z, stream));
-  HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, topk_idx, topk_w, probs, stream),
+  HIP_TRY(launch_softmax_topk(z, (int)p.T, p.E, p.k, p.renorm ? 1 : 0, topk_idx, topk_w, probs, stream,
+                              p.gate_ksplit),
           "softmax/top-k");
   return MOE_OK;
 }

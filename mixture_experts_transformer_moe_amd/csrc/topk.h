@@ -57,13 +57,14 @@ __device__ inline void wave_topk_only(const float* z, int E, int k, int* idx_out
     for (int j = 0; j < k; ++j) idx_out[j] = sel[j];
 }
 
-// z: this token's E logits (fp32). Writes idx_out[0..k), w_out[0..k) and, when
+// z: this token's E logits (fp32), or nsplit partial sums of them nstride floats
+// apart, added in order 0, 1, ... . Writes idx_out[0..k), w_out[0..k) and, when
 // probs != null, probs[0..E). Softmax is max-subtracted fp32; the choice is made
 // on the logits (ties to the lower expert index), so exp rounding cannot tie.
 // Every lane returns the chosen indices in sel[0..k).
 __device__ inline void wave_softmax_topk(const float* z, int E, int k, bool renorm,
                                          float* probs, int* idx_out, float* w_out,
-                                         int* sel) {
+                                         int* sel, int nsplit = 1, long long nstride = 0) {
   const int lane = lane_id();
   float v[MOE_MAX_EPL];
   const int epl = (E + MOE_WAVE - 1) / MOE_WAVE;
@@ -71,7 +72,12 @@ __device__ inline void wave_softmax_topk(const float* z, int E, int k, bool reno
 #pragma unroll
   for (int i = 0; i < MOE_MAX_EPL; ++i) {
     int e = lane + i * MOE_WAVE;
-    v[i] = (i < epl && e < E) ? z[e] : -INFINITY;
+    float a = -INFINITY;
+    if (i < epl && e < E) {
+      a = z[e];
+      for (int s = 1; s < nsplit; ++s) a += z[s * nstride + e];
+    }
+    v[i] = a;
     m = fmaxf(m, v[i]);
   }
   m = wave_max(m);
