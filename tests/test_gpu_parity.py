@@ -62,6 +62,10 @@ CASES = {
     # sixteen dispatch blocks with one expert, and eighteen with 32 experts, top-2
     "gemm_multi_e8": W.LayerShape("gm8", T=16384, H=64, F=128, E=8, E_loc=8, k=1, cf=1.0, dtype="f16"),
     "gemm_multi_block": W.LayerShape("gmb", T=9000, H=128, F=256, E=32, E_loc=32, k=2, cf=1.0, dtype="f16"),
+    # matrix-core gate with K in four slices (H = 2048: 32 steps of 128 bytes),
+    # fp32 partial logits summed by the softmax / top-k, probabilities included
+    "gate_k_slices": W.LayerShape("gks", T=512, H=2048, F=256, E=64, E_loc=8, e_lo=8, k=2, cf=1.0, dtype="f16"),
+    "gate_k_slices_bf16": W.LayerShape("gksb", T=300, H=1024, F=256, E=128, E_loc=16, k=1, cf=1.0, dtype="bf16"),
 }
 
 
