@@ -80,12 +80,19 @@ __device__ inline int xcd_remap(int i, int total) {
 
 template <typename BiasT>
 __device__ inline float load_bias(const BiasT* b, int n);
+// (global address space stated: the bias may come from a per-segment pointer table)
 template <>
-__device__ inline float load_bias<float>(const float* b, int n) { return b[n]; }
+__device__ inline float load_bias<float>(const float* b, int n) {
+  return ((const __attribute__((address_space(1))) float*)b)[n];
+}
 template <>
-__device__ inline float load_bias<_Float16>(const _Float16* b, int n) { return (float)b[n]; }
+__device__ inline float load_bias<_Float16>(const _Float16* b, int n) {
+  return (float)((const __attribute__((address_space(1))) _Float16*)b)[n];
+}
 template <>
-__device__ inline float load_bias<__bf16>(const __bf16* b, int n) { return (float)b[n]; }
+__device__ inline float load_bias<__bf16>(const __bf16* b, int n) {
+  return (float)((const __attribute__((address_space(1))) __bf16*)b)[n];
+}
 
 // Epilogue of a wave's TN x TM accumulator tiles: lane holds
 // D[n = n0 + 16 i + 4 (lane / 16) + q][m = m0 + 16 j + lane % 16], q = 0..3;
@@ -249,14 +256,17 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   const int frag_c0 = (((lane >> 4)) ^ (frag_row & 7)) * 16;
   const int frag_c1 = ((4 + (lane >> 4)) ^ (frag_row & 7)) * 16;
 
-// global -> registers RA/RB for stage KS (all loads of the stage in flight together)
+// global -> registers RA/RB for stage KS (all loads of the stage in flight together).
+// The operands are global memory: said so, the loads are global_load (a flat
+// load would also count against lgkmcnt, and every LDS wait would then wait for
+// the stage in flight too)
 #define GEMM_GLOAD(RA, RB, KS)                                                           \
   {                                                                                      \
     const long long off_ = (long long)(KS) * 128;                                        \
     _Pragma("unroll") for (int i = 0; i < ACH; ++i) RA[i] =                              \
-        *reinterpret_cast<const u32x4_t*>(a_src[i] + off_);                              \
+        *(const __attribute__((address_space(1))) u32x4_t*)(a_src[i] + off_);           \
     _Pragma("unroll") for (int i = 0; i < BCH; ++i) RB[i] =                              \
-        *reinterpret_cast<const u32x4_t*>(b_src[i] + off_);                              \
+        *(const __attribute__((address_space(1))) u32x4_t*)(b_src[i] + off_);           \
   }
 // registers RA/RB -> LDS buffer BUF
 #define GEMM_LSTORE(RA, RB, BUF)                                                         \
