@@ -278,20 +278,35 @@ __device__ inline bool route_phase2(const RouteParams& rp, const RouteLds& L, in
   return seg >= 0;
 }
 
+// Loads whose address space the compiler cannot see through a pointer table or
+// a pointer that may hold LDS are stated explicitly: a flat load also counts
+// against lgkmcnt, and waiting for it would drain the weight loads in flight.
+template <typename X>
+__device__ inline X gload(const X* p) { return *(const __attribute__((address_space(1))) X*)p; }
+__device__ inline int lds_load(const int* p) { return *(const __attribute__((address_space(3))) int*)p; }
+
+// Every small load a work-group's epilogue needs (activation row indices, bias,
+// the row's token and gate weight) is issued before or with the weight loads,
+// so only the weight stream itself is left to wait for.
 template <typename DT, int MAXM, int NQ>
 __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p, RouteParams rp) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
   constexpr int N = RPW * MAXM;
+  constexpr int SH = 6 - ilog2(N);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nchunk = p.F / (UP_WAVES * RPW);
   const int g = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - g * nchunk;
-  const int* a_rows = p.a_rows;
   const long long H = p.H, F = p.F;
   const int f0 = chunk * UP_WAVES * RPW + wave * RPW;
+  // after the reduction lane l holds value v = l >> SH: weight row f0 + oi, activation row om
+  const int v = lane >> SH;
+  const int oi = v / MAXM, om = v - (v / MAXM) * MAXM;
   uint4 wv[RPW][NQ];
+  int rows[MAXM];
+  T bias_raw = DT::from_f(0.f);
   int seg = 0, r0 = 0, r1 = p.M;
   if (rp.z) {
     // routed here: work-group g serves assignment g; its weight loads go out as
@@ -301,17 +316,31 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p
     const int e = route_phase1(rp, L, g);
     if (e >= 0) {
       const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[e]) : reinterpret_cast<const T*>(p.w1) + (long long)e * F * H;
+      const T* b1s = p.b1p ? reinterpret_cast<const T*>(p.b1p[e]) : reinterpret_cast<const T*>(p.b1) + (long long)e * F;
       load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H, H);
+      bias_raw = gload(b1s + f0 + oi);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (!route_phase2(rp, L, p.H, g, seg, r0, r1, a_rows)) return;   // leads a segment: seg == e
+    const int* lst;
+    if (!route_phase2(rp, L, p.H, g, seg, r0, r1, lst)) return;   // leads a segment: seg == e
+    const int M = min(r1 - r0, MAXM);
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) rows[m] = lds_load(lst + r0 + (m < M ? m : 0));
   } else {
     if (p.seg_off) {
       if (!find_active(p.seg_off, p.nseg, g, seg, r0, r1)) return;
     } else if (g > 0) {
       return;
     }
+    const int M = min(r1 - r0, MAXM);
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      const int r = r0 + (m < M ? m : 0);
+      rows[m] = p.a_rows ? gload(p.a_rows + r) : r;
+    }
     const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[seg]) : reinterpret_cast<const T*>(p.w1) + (long long)seg * F * H;
+    const T* b1s = p.b1p ? reinterpret_cast<const T*>(p.b1p[seg]) : reinterpret_cast<const T*>(p.b1) + (long long)seg * F;
+    bias_raw = gload(b1s + f0 + oi);
     load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H, H);
     __builtin_amdgcn_sched_barrier(0);   // every weight load is in flight before anything else
   }
@@ -319,19 +348,11 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p
   const T* x = reinterpret_cast<const T*>(p.x);
   const T* act[MAXM];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
-    const int r = r0 + (m < M ? m : 0);
-    const long long row = a_rows ? (long long)a_rows[r] : (long long)r;
-    act[m] = x + row * H;
-  }
+  for (int m = 0; m < MAXM; ++m) act[m] = x + (long long)rows[m] * H;
   const float s = dot_rows<DT, MAXM, NQ, RPW>(wv, act);
-  constexpr int SH = 6 - ilog2(N);
-  const int v = lane >> SH;
-  const int i = v / MAXM, m = v - (v / MAXM) * MAXM;
-  if ((lane & ((1 << SH) - 1)) == 0 && m < M) {
-    const T* b1 = p.b1p ? reinterpret_cast<const T*>(p.b1p[seg]) : reinterpret_cast<const T*>(p.b1) + (long long)seg * F;
-    const float u = s + DT::to_f(b1[f0 + i]);
-    reinterpret_cast<T*>(p.h)[(long long)(r0 + m) * F + f0 + i] = DT::from_f(pin_f32(gelu_erf(u)));
+  if ((lane & ((1 << SH) - 1)) == 0 && om < M) {
+    const float u = s + DT::to_f(bias_raw);
+    reinterpret_cast<T*>(p.h)[(long long)(r0 + om) * F + f0 + oi] = DT::from_f(pin_f32(gelu_erf(u)));
   }
 }
 
@@ -340,6 +361,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
   constexpr int N = RPW * MAXM;
+  constexpr int SH = 6 - ilog2(N);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nchunk = p.H / (4 * RPW);
@@ -353,28 +375,33 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p) {
   }
   const long long H = p.H, F = p.F;
   const int j0 = chunk * 4 * RPW + wave * RPW;
+  const int M = min(r1 - r0, MAXM);
+  const int v = lane >> SH;
+  const int oi = v / MAXM, om = v - (v / MAXM) * MAXM;
+  const T* b2s = p.b2p ? reinterpret_cast<const T*>(p.b2p[seg]) : reinterpret_cast<const T*>(p.b2) + (long long)seg * H;
+  const T bias_raw = gload(b2s + j0 + oi);
+  int t_out = 0;
+  if (FUSE) t_out = gload(p.slot_token + r0 + (om < M ? om : M - 1));   // a kept row: a token
   uint4 wv[RPW][NQ];
   const T* w2s = p.w2p ? reinterpret_cast<const T*>(p.w2p[seg]) : reinterpret_cast<const T*>(p.w2) + (long long)seg * H * F;
   load_rows<DT, NQ, RPW>(wv, w2s + (long long)j0 * F, F);
   __builtin_amdgcn_sched_barrier(0);
-  const int M = min(r1 - r0, MAXM);
+  float wt = 0.f;
+  if (FUSE) {   // issued here, not after the dot: the token is back long before the weights
+    wt = gload(p.topk_w + t_out);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const T* h = reinterpret_cast<const T*>(p.h);
   const T* act[MAXM];
 #pragma unroll
   for (int m = 0; m < MAXM; ++m) act[m] = h + (long long)(r0 + (m < M ? m : 0)) * F;
   const float s = dot_rows<DT, MAXM, NQ, RPW>(wv, act);
-  constexpr int SH = 6 - ilog2(N);
-  const int v = lane >> SH;
-  const int i = v / MAXM, m = v - (v / MAXM) * MAXM;
-  if ((lane & ((1 << SH) - 1)) == 0 && m < M) {
-    const T* b2 = p.b2p ? reinterpret_cast<const T*>(p.b2p[seg]) : reinterpret_cast<const T*>(p.b2) + (long long)seg * H;
-    const float yv = s + DT::to_f(b2[j0 + i]);
+  if ((lane & ((1 << SH) - 1)) == 0 && om < M) {
+    const float yv = s + DT::to_f(bias_raw);
     if (FUSE) {
-      const int t = p.slot_token[r0 + m];
-      const float wt = p.topk_w[t];
-      reinterpret_cast<T*>(p.out)[(long long)t * H + j0 + i] = DT::from_f(pin_f32(fmaf(wt, yv, 0.f)));
+      reinterpret_cast<T*>(p.out)[(long long)t_out * H + j0 + oi] = DT::from_f(pin_f32(fmaf(wt, yv, 0.f)));
     } else {
-      reinterpret_cast<float*>(p.out)[(long long)(r0 + m) * H + j0 + i] = yv;
+      reinterpret_cast<float*>(p.out)[(long long)(r0 + om) * H + j0 + oi] = yv;
     }
   }
 }
