@@ -194,6 +194,10 @@ struct GemmParams {
   // writes its partial sums to C + s * c_split (bias in slice 0 only); 0 or 1: none
   int ksplit;
   long long c_split;
+  // host only: every weight tile is read by a single work-group (segments of at
+  // most one row tile), so the launch picks the variant that streams the
+  // weights with non-temporal loads
+  int stream_w;
 };
 
 // Expert FFN for segments of at most MAXM rows: each work-group takes one

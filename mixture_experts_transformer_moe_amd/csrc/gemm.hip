@@ -173,7 +173,7 @@ __device__ inline bool gemm_tile(const GemmParams& p, int BM, int& seg, int& nt,
 // NTH threads (4 or 8 waves, laid out WM x WN over the tile); DEPTH stages of
 // global loads in flight; the launch bound asks for two waves per SIMD when the
 // registers of two stages or of eight waves must fit.
-template <typename DT, int BM, int BN, int EPI, typename BiasT, int DEPTH, int NTH>
+template <typename DT, int BM, int BN, int EPI, typename BiasT, int DEPTH, int NTH, bool WNT>
 __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped_gemm_kernel(GemmParams p) {
   using T = typename DT::T;
   constexpr int NW = NTH / 64;
@@ -259,14 +259,18 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 // global -> registers RA/RB for stage KS (all loads of the stage in flight together).
 // The operands are global memory: said so, the loads are global_load (a flat
 // load would also count against lgkmcnt, and every LDS wait would then wait for
-// the stage in flight too)
+// the stage in flight too). W_: the weights are read once, non-temporally.
 #define GEMM_GLOAD(RA, RB, KS)                                                           \
   {                                                                                      \
     const long long off_ = (long long)(KS) * 128;                                        \
     _Pragma("unroll") for (int i = 0; i < ACH; ++i) RA[i] =                              \
         *(const __attribute__((address_space(1))) u32x4_t*)(a_src[i] + off_);           \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i) RB[i] =                              \
-        *(const __attribute__((address_space(1))) u32x4_t*)(b_src[i] + off_);           \
+    _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                    \
+      const __attribute__((address_space(1))) u32x4_t* q_ =                              \
+          (const __attribute__((address_space(1))) u32x4_t*)(b_src[i] + off_);           \
+      if constexpr (W_) RB[i] = __builtin_nontemporal_load(q_);                          \
+      else RB[i] = *q_;                                                                  \
+    }                                                                                    \
   }
 // registers RA/RB -> LDS buffer BUF
 #define GEMM_LSTORE(RA, RB, BUF)                                                         \
@@ -296,62 +300,74 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   }
 #define GEMM_SB __builtin_amdgcn_sched_barrier(0)
 
-  if constexpr (DEPTH == 1) {
-    // one stage in flight: stage ks + 1 loads while stage ks is multiplied
-    u32x4_t ra[ACH], rb[BCH];
-    GEMM_GLOAD(ra, rb, 0);
-    GEMM_LSTORE(ra, rb, 0);
-    __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-      const int buf = ks & 1;
-      if (ks + 1 < nk) GEMM_GLOAD(ra, rb, ks + 1);
-      GEMM_MATH(buf);
-      if (ks + 1 < nk) GEMM_LSTORE(ra, rb, buf ^ 1);
+  // The K loop, with or without non-temporal weight loads. With WNT the expert
+  // tiles stream their weights (each tile read by this work-group only) and the
+  // extra segment's tiles, which all read the same dense weights, keep them cached.
+  auto k_loop = [&](auto stream_tag) {
+    constexpr bool W_ = decltype(stream_tag)::value;
+    if constexpr (DEPTH == 1) {
+      // one stage in flight: stage ks + 1 loads while stage ks is multiplied
+      u32x4_t ra[ACH], rb[BCH];
+      GEMM_GLOAD(ra, rb, 0);
+      GEMM_LSTORE(ra, rb, 0);
       __syncthreads();
-    }
-  } else {
-    // two stages in flight (register ping-pong): while stage c is multiplied from
-    // LDS, stages c + 1 and c + 2 are loading. Stage c sits in LDS buffer c & 1;
-    // stage c + 1 in register set (c + 1) & 1. The steady loop's loads are
-    // unconditional so the wait for one register set leaves the other in flight.
-    u32x4_t ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
-    GEMM_GLOAD(ra0, rb0, 0);
-    GEMM_SB;
-    if (nk > 1) GEMM_GLOAD(ra1, rb1, 1);
-    GEMM_SB;
-    GEMM_LSTORE(ra0, rb0, 0);
-    if (nk > 2) GEMM_GLOAD(ra0, rb0, 2);
-    GEMM_SB;
-    __syncthreads();
-    int c = 0;
-    for (; c + 4 < nk; c += 2) {   // LDS buf 0 = stage c, set 1 = stage c + 1, set 0 = stage c + 2
-      GEMM_MATH(0);
-      GEMM_LSTORE(ra1, rb1, 1);
-      GEMM_GLOAD(ra1, rb1, c + 3);
-      GEMM_SB;
-      __syncthreads();
-      GEMM_MATH(1);
-      GEMM_LSTORE(ra0, rb0, 0);
-      GEMM_GLOAD(ra0, rb0, c + 4);
-      GEMM_SB;
-      __syncthreads();
-    }
-    for (; c < nk; ++c) {          // the last (at most four) stages
-      if ((c & 1) == 0) {
-        GEMM_MATH(0);
-        if (c + 1 < nk) {
-          GEMM_LSTORE(ra1, rb1, 1);
-          if (c + 3 < nk) GEMM_GLOAD(ra1, rb1, c + 3);
-        }
-      } else {
-        GEMM_MATH(1);
-        if (c + 1 < nk) {
-          GEMM_LSTORE(ra0, rb0, 0);
-          if (c + 3 < nk) GEMM_GLOAD(ra0, rb0, c + 3);
-        }
+      for (int ks = 0; ks < nk; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nk) GEMM_GLOAD(ra, rb, ks + 1);
+        GEMM_MATH(buf);
+        if (ks + 1 < nk) GEMM_LSTORE(ra, rb, buf ^ 1);
+        __syncthreads();
       }
+    } else {
+      // two stages in flight (register ping-pong): while stage c is multiplied from
+      // LDS, stages c + 1 and c + 2 are loading. Stage c sits in LDS buffer c & 1;
+      // stage c + 1 in register set (c + 1) & 1. The steady loop's loads are
+      // unconditional so the wait for one register set leaves the other in flight.
+      u32x4_t ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
+      GEMM_GLOAD(ra0, rb0, 0);
+      GEMM_SB;
+      if (nk > 1) GEMM_GLOAD(ra1, rb1, 1);
+      GEMM_SB;
+      GEMM_LSTORE(ra0, rb0, 0);
+      if (nk > 2) GEMM_GLOAD(ra0, rb0, 2);
+      GEMM_SB;
       __syncthreads();
+      int c = 0;
+      for (; c + 4 < nk; c += 2) {   // LDS buf 0 = stage c, set 1 = stage c + 1, set 0 = stage c + 2
+        GEMM_MATH(0);
+        GEMM_LSTORE(ra1, rb1, 1);
+        GEMM_GLOAD(ra1, rb1, c + 3);
+        GEMM_SB;
+        __syncthreads();
+        GEMM_MATH(1);
+        GEMM_LSTORE(ra0, rb0, 0);
+        GEMM_GLOAD(ra0, rb0, c + 4);
+        GEMM_SB;
+        __syncthreads();
+      }
+      for (; c < nk; ++c) {          // the last (at most four) stages
+        if ((c & 1) == 0) {
+          GEMM_MATH(0);
+          if (c + 1 < nk) {
+            GEMM_LSTORE(ra1, rb1, 1);
+            if (c + 3 < nk) GEMM_GLOAD(ra1, rb1, c + 3);
+          }
+        } else {
+          GEMM_MATH(1);
+          if (c + 1 < nk) {
+            GEMM_LSTORE(ra0, rb0, 0);
+            if (c + 3 < nk) GEMM_GLOAD(ra0, rb0, c + 3);
+          }
+        }
+        __syncthreads();
+      }
     }
+  };
+  if constexpr (WNT) {
+    if (extra) k_loop(std::false_type{});
+    else k_loop(std::true_type{});
+  } else {
+    k_loop(std::false_type{});
   }
 #undef GEMM_GLOAD
 #undef GEMM_LSTORE
@@ -398,8 +414,17 @@ template <typename DT, int BM, int BN, int EPI, typename BiasT>
 static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   constexpr int NTH = BN == 256 ? 512 : GEMM_THREADS;
   constexpr int DEPTH = (BM <= 64 || (NTH == 512 && BM == 128)) ? 2 : 1;
-  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH>), dim3(grid, p.ksplit > 1 ? p.ksplit : 1),
-             dim3(NTH), 0, s, ev.start, ev.stop, p);
+  const dim3 g(grid, p.ksplit > 1 ? p.ksplit : 1);
+  // (float bias: the gate's logits, whose weight tile every token tile reads)
+  if constexpr (BM <= 64 && !std::is_same<BiasT, float>::value) {
+    if (p.stream_w) {   // weight streaming tiles (segments of one row tile)
+      MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, true>), g, dim3(NTH), 0, s, ev.start,
+                 ev.stop, p);
+      return;
+    }
+  }
+  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, false>), g, dim3(NTH), 0, s, ev.start, ev.stop,
+             p);
 }
 
 template <typename DT, int BM, int BN>

@@ -94,6 +94,7 @@ struct Plan {
   bool residual, renorm;
   // gate
   bool gate_mfma;
+  bool stream_w;       // expert GEMMs: each weight tile read by one work-group (non-temporal weight loads)
   int gate_BM, gate_BN;
   int gate_ksplit;     // matrix-core gate: slices of K, each writing fp32 partial logits
   // dispatch
@@ -223,6 +224,10 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   // streaming). With smaller expert tiles the MLP would run on tiles too thin
   // for its T rows (measured slower), so it keeps its own launches.
   p.dense_in_experts = p.residual && !p.exp_decode && !p.dense_decode && p.BM >= 64;
+  // every segment fits one row tile: each expert weight tile is read by one
+  // work-group, so the GEMMs stream the expert weights past the caches (the
+  // dense MLP's tiles in the same launches keep theirs cached)
+  p.stream_w = !p.exp_decode && seg_rows <= p.BM;
   if (p.dense_in_experts) {
     const int64_t mte = (p.T + p.BM - 1) / p.BM;
     if (mte >= 65536) return fail(MOE_ERR_UNSUPPORTED, "too many row tiles");
@@ -446,6 +451,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g1.tiles = l1;
   g1.tile_count = cnt;
   g1.n_ntiles = nt1;
+  g1.stream_w = p.stream_w ? 1 : 0;
   if (dense) {   // the residual MLP over all T tokens: h_dense = GeLU(x W1_mlp^T + b1_mlp)
     g1.A2 = x;
     g1.B2 = w->mlp_w1;
@@ -472,6 +478,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g2.tiles = l2;
   g2.tile_count = cnt;
   g2.n_ntiles = nt2;
+  g2.stream_w = p.stream_w ? 1 : 0;
   if (dense) {   // m = h_dense W2_mlp^T + b2_mlp, fp32
     g2.A2 = wsp<void>(ws, p.o_dh);
     g2.B2 = w->mlp_w2;
