@@ -194,9 +194,9 @@ struct GemmParams {
   // writes its partial sums to C + s * c_split (bias in slice 0 only); 0 or 1: none
   int ksplit;
   long long c_split;
-  // host only: every weight tile is read by a single work-group (segments of at
-  // most one row tile), so the launch picks the variant that streams the
-  // weights with non-temporal loads
+  // host only: every expert weight tile is read by at most two work-groups
+  // (segments of at most two row tiles), so the launch picks the variant that
+  // streams the expert weights with non-temporal loads
   int stream_w;
 };
 

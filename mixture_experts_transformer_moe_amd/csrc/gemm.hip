@@ -415,9 +415,10 @@ static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) 
   constexpr int NTH = BN == 256 ? 512 : GEMM_THREADS;
   constexpr int DEPTH = (BM <= 64 || (NTH == 512 && BM == 128)) ? 2 : 1;
   const dim3 g(grid, p.ksplit > 1 ? p.ksplit : 1);
-  // (float bias: the gate's logits, whose weight tile every token tile reads)
-  if constexpr (BM <= 64 && !std::is_same<BiasT, float>::value) {
-    if (p.stream_w) {   // weight streaming tiles (segments of one row tile)
+  // (float bias: the gate's logits, whose weight tile every token tile reads;
+  // the two-stage 128 x 256 tile has no registers left for a second loop copy)
+  if constexpr (!std::is_same<BiasT, float>::value && !(BM == 128 && BN == 256)) {
+    if (p.stream_w) {   // expert weights read by one or two row tiles each
       MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, true>), g, dim3(NTH), 0, s, ev.start,
                  ev.stop, p);
       return;
