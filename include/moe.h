@@ -227,7 +227,8 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
  * expert kernels read a cached expert from its slot and any other expert
  * directly from pinned host memory over the host link, only when the routing
  * selects it. create / destroy / set_expert synchronise the device (set-up
- * calls); update only enqueues work. Use one store from one stream at a time. */
+ * calls); update, update_async and commit only enqueue work. Use one store from
+ * one compute stream at a time. */
 typedef struct moe_expert_store* moe_expert_store_t;
 
 /* Allocates the store for descriptor d (pinned host memory for E_loc experts,
@@ -258,8 +259,29 @@ moe_status_t moe_expert_store_weights(moe_expert_store_t store, moe_layer_weight
 moe_status_t moe_expert_store_update(moe_expert_store_t store, const int32_t* demand /* host */,
                                      hipStream_t stream, int32_t* copied /* host */);
 
+/* The same choice as moe_expert_store_update, with the copies on copy_stream so
+ * that they overlap with work enqueued on stream meanwhile (MoE-MPMC summary:
+ * expert loads overlapped with inference). Enqueued: on stream, leaving experts
+ * switch to host reads; copy_stream waits for that point of stream and copies
+ * the incoming experts into their slots. Until moe_expert_store_commit, every
+ * incoming expert is still read from host memory, so results never depend on
+ * when the copies finish. A pending asynchronous update is committed (on
+ * stream) by the next update, update_async or commit. copy_stream must differ
+ * from stream; the library creates no stream (give both the default priority).
+ * Errors: INVALID_ARGUMENT (NULL store or demand, equal streams, negative
+ * demand), MOE_ERR_HIP. */
+moe_status_t moe_expert_store_update_async(moe_expert_store_t store, const int32_t* demand /* host */,
+                                           hipStream_t stream, hipStream_t copy_stream,
+                                           int32_t* copied /* host */);
+
+/* Ends a pending update_async: stream waits for its copies, then the copied
+ * experts switch to slot reads for the work enqueued after. Nothing pending: a
+ * no-op. */
+moe_status_t moe_expert_store_commit(moe_expert_store_t store, hipStream_t stream);
+
 /* slot_of[i] (HOST array [E_loc]) = device slot of local expert i, or -1 if it
- * is read from host memory, as of the last update call. */
+ * is read from host memory, as chosen by the last update call (after an
+ * update_async, reads switch to the slot at the commit). */
 moe_status_t moe_expert_store_residency(moe_expert_store_t store, int32_t* slot_of /* host */);
 
 /* Static text for a status code. */

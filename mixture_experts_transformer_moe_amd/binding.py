@@ -26,7 +26,8 @@ EXPORTED = ["moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_layer_pla
             "moe_expert_ffn", "moe_dense_ffn", "moe_combine", "moe_layer_forward",
             "moe_layer_forward_ex", "moe_status_str", "moe_last_error",
             "moe_expert_store_create", "moe_expert_store_destroy", "moe_expert_store_set_expert",
-            "moe_expert_store_weights", "moe_expert_store_update", "moe_expert_store_residency"]
+            "moe_expert_store_weights", "moe_expert_store_update", "moe_expert_store_update_async",
+            "moe_expert_store_commit", "moe_expert_store_residency"]
 
 _DTYPE_CODE = {torch.float32: MOE_DTYPE_F32, torch.float16: MOE_DTYPE_F16, torch.bfloat16: MOE_DTYPE_BF16}
 _DTYPE_NAME = {"f32": MOE_DTYPE_F32, "f16": MOE_DTYPE_F16, "bf16": MOE_DTYPE_BF16}
@@ -117,6 +118,10 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_store_weights.argtypes = [P, W]
         L.moe_expert_store_update.restype = st
         L.moe_expert_store_update.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_int32)]
+        L.moe_expert_store_update_async.restype = st
+        L.moe_expert_store_update_async.argtypes = [P, P, P, P, ctypes.POINTER(ctypes.c_int32)]
+        L.moe_expert_store_commit.restype = st
+        L.moe_expert_store_commit.argtypes = [P, P]
         L.moe_expert_store_residency.restype = st
         L.moe_expert_store_residency.argtypes = [P, P]
         L.moe_status_str.restype = ctypes.c_char_p
@@ -300,6 +305,20 @@ class ExpertStore:
         n = ctypes.c_int32(0)
         _check(lib().moe_expert_store_update(self.handle, d.ctypes.data, _stream(stream), ctypes.byref(n)))
         return n.value
+
+    def update_async(self, demand, copy_stream, stream=None) -> int:
+        """The same choice with the copies on copy_stream (see commit); returns experts copied."""
+        d = np.ascontiguousarray(np.asarray(demand, dtype=np.int32))
+        if d.shape != (self.shape.E,):
+            raise ValueError("demand must have one entry per global expert")
+        n = ctypes.c_int32(0)
+        _check(lib().moe_expert_store_update_async(self.handle, d.ctypes.data, _stream(stream), _stream(copy_stream),
+                                                   ctypes.byref(n)))
+        return n.value
+
+    def commit(self, stream=None) -> None:
+        """stream waits for the copies of a pending update_async; the copied experts switch to their slots."""
+        _check(lib().moe_expert_store_commit(self.handle, _stream(stream)))
 
     def residency(self) -> np.ndarray:
         out = np.zeros(self.shape.E_loc, dtype=np.int32)

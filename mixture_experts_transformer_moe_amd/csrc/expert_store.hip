@@ -18,6 +18,13 @@
 // memory, (2) the newly cached experts are copied into their slots, (3) their
 // pointers switch to the slots. Work enqueued earlier on the stream still reads
 // the old placement; work enqueued later sees the new one.
+//
+// moe_expert_store_update_async() puts step (2) on a copy stream that first
+// waits for step (1) on the compute stream, so the copies overlap with the
+// layers enqueued meanwhile (which read the incoming experts from host memory,
+// as before); moe_expert_store_commit() later makes the compute stream wait for
+// the copies and enqueues step (3). A freed slot is only written after every
+// read of it enqueued before step (1), and only read after step (3).
 #include <math.h>
 #include <string.h>
 
@@ -62,6 +69,10 @@ struct moe_expert_store {
   std::vector<int> expert_in;        // slot -> local expert, -1 = free
   std::vector<double> score;         // decayed demand
   double decay = 0.5;
+  hipEvent_t evicted = nullptr;      // recorded on the compute stream after step (1)
+  hipEvent_t copied = nullptr;       // recorded on the copy stream after step (2)
+  bool pending = false;              // an asynchronous update awaits its commit
+  std::vector<std::pair<int, const void*>> pending_place;
 };
 
 namespace {
@@ -97,6 +108,8 @@ void placement_updates(const moe_expert_store* s, int e, bool on_device, int slo
 }
 
 void release(moe_expert_store* s) {
+  if (s->evicted) (void)hipEventDestroy(s->evicted);
+  if (s->copied) (void)hipEventDestroy(s->copied);
   if (s->tables) (void)hipFree((void*)s->tables);
   if (s->dev) (void)hipFree(s->dev);
   if (s->host) (void)hipHostFree(s->host);
@@ -146,6 +159,9 @@ moe_status_t moe_expert_store_create(const moe_layer_desc_t* d, int32_t slots, m
   }
   e = hipMalloc((void**)&s->tables, sizeof(void*) * 4 * s->E_loc);
   if (e != hipSuccess) { release(s); return api_error(MOE_ERR_HIP, hipGetErrorString(e)); }
+  e = hipEventCreateWithFlags(&s->evicted, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&s->copied, hipEventDisableTiming);
+  if (e != hipSuccess) { release(s); return api_error(MOE_ERR_HIP, hipGetErrorString(e)); }
   for (int i = 0; i < s->E_loc; ++i)
     for (int part = 0; part < 4; ++part) s->shadow[part * s->E_loc + i] = expert_part(s, false, i, part);
   e = hipMemcpy((void*)s->tables, s->shadow.data(), sizeof(void*) * 4 * s->E_loc, hipMemcpyHostToDevice);
@@ -193,14 +209,18 @@ moe_status_t moe_expert_store_weights(moe_expert_store_t s, moe_layer_weights_t*
   return MOE_OK;
 }
 
-moe_status_t moe_expert_store_update(moe_expert_store_t s, const int32_t* demand, hipStream_t stream,
-                                     int32_t* copied) {
-  if (!s || !demand) return api_error(MOE_ERR_INVALID_ARGUMENT, "store or demand is NULL");
-  for (int i = 0; i < s->E_loc; ++i) {
-    const int32_t c = demand[s->e_lo + i];
-    if (c < 0) return api_error(MOE_ERR_INVALID_ARGUMENT, "negative demand");
-    s->score[i] = s->decay * s->score[i] + c;
-  }
+}  // extern "C"
+
+namespace {
+
+// Folds demand into the scores and moves the placement to the `slots` best
+// experts (host bookkeeping only): evict gets the pointer updates of leaving
+// experts, moves the (expert, slot) pairs to copy, place their pointer updates.
+moe_status_t choose(moe_expert_store* s, const int32_t* demand, std::vector<std::pair<int, const void*>>& evict,
+                    std::vector<std::pair<int, int>>& moves, std::vector<std::pair<int, const void*>>& place) {
+  for (int i = 0; i < s->E_loc; ++i)
+    if (demand[s->e_lo + i] < 0) return api_error(MOE_ERR_INVALID_ARGUMENT, "negative demand");
+  for (int i = 0; i < s->E_loc; ++i) s->score[i] = s->decay * s->score[i] + demand[s->e_lo + i];
   // the `slots` highest scores (ties to the lower expert), demanded at least once
   std::vector<int> order(s->E_loc);
   for (int i = 0; i < s->E_loc; ++i) order[i] = i;
@@ -208,9 +228,6 @@ moe_status_t moe_expert_store_update(moe_expert_store_t s, const int32_t* demand
   std::vector<char> want(s->E_loc, 0);
   for (int r = 0; r < s->slots && r < s->E_loc; ++r)
     if (s->score[order[r]] > 0) want[order[r]] = 1;
-
-  std::vector<std::pair<int, const void*>> evict, place;
-  std::vector<int> incoming;
   for (int sl = 0; sl < s->slots; ++sl) {
     const int e = s->expert_in[sl];
     if (e >= 0 && !want[e]) {
@@ -219,28 +236,78 @@ moe_status_t moe_expert_store_update(moe_expert_store_t s, const int32_t* demand
       s->expert_in[sl] = -1;
     }
   }
-  for (int e = 0; e < s->E_loc; ++e)
-    if (want[e] && s->slot_of[e] < 0) incoming.push_back(e);
-  // (1) leaving experts read from host memory from here on
-  moe_status_t st = push_updates(s, evict, stream);
-  if (st != MOE_OK) return st;
-  // (2) copy the incoming experts into free slots (stream order: after every earlier use of the slot)
   int sl = 0;
-  for (int e : incoming) {
+  for (int e = 0; e < s->E_loc; ++e) {
+    if (!want[e] || s->slot_of[e] >= 0) continue;
     while (sl < s->slots && s->expert_in[sl] >= 0) ++sl;
     if (sl >= s->slots) break;
-    const hipError_t err = hipMemcpyAsync((void*)expert_part(s, true, sl, 0), expert_part(s, false, e, 0),
-                                          s->expert_bytes, hipMemcpyHostToDevice, stream);
-    if (err != hipSuccess) return api_error(MOE_ERR_HIP, hipGetErrorString(err));
     s->expert_in[sl] = e;
     s->slot_of[e] = sl;
+    moves.emplace_back(e, sl);
     placement_updates(s, e, true, sl, place);
   }
-  // (3) the copied experts read from their slots from here on
-  st = push_updates(s, place, stream);
-  if (st != MOE_OK) return st;
-  if (copied) *copied = (int32_t)(place.size() / 4);
   return MOE_OK;
+}
+
+moe_status_t copy_in(moe_expert_store* s, const std::vector<std::pair<int, int>>& moves, hipStream_t stream) {
+  for (const auto& m : moves) {
+    const hipError_t err = hipMemcpyAsync((void*)expert_part(s, true, m.second, 0), expert_part(s, false, m.first, 0),
+                                          s->expert_bytes, hipMemcpyHostToDevice, stream);
+    if (err != hipSuccess) return api_error(MOE_ERR_HIP, hipGetErrorString(err));
+  }
+  return MOE_OK;
+}
+
+moe_status_t commit(moe_expert_store* s, hipStream_t stream) {
+  if (!s->pending) return MOE_OK;
+  const hipError_t err = hipStreamWaitEvent(stream, s->copied, 0);
+  if (err != hipSuccess) return api_error(MOE_ERR_HIP, hipGetErrorString(err));
+  s->pending = false;
+  return push_updates(s, s->pending_place, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_expert_store_update(moe_expert_store_t s, const int32_t* demand, hipStream_t stream,
+                                     int32_t* copied) {
+  if (!s || !demand) return api_error(MOE_ERR_INVALID_ARGUMENT, "store or demand is NULL");
+  MOE_RETURN_IF_ERROR(commit(s, stream));
+  std::vector<std::pair<int, const void*>> evict, place;
+  std::vector<std::pair<int, int>> moves;
+  MOE_RETURN_IF_ERROR(choose(s, demand, evict, moves, place));
+  MOE_RETURN_IF_ERROR(push_updates(s, evict, stream));   // (1) leaving experts read from host memory from here on
+  MOE_RETURN_IF_ERROR(copy_in(s, moves, stream));        // (2) after every earlier use of the freed slots (stream order)
+  MOE_RETURN_IF_ERROR(push_updates(s, place, stream));   // (3) the copied experts read from their slots from here on
+  if (copied) *copied = (int32_t)moves.size();
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_store_update_async(moe_expert_store_t s, const int32_t* demand, hipStream_t stream,
+                                           hipStream_t copy_stream, int32_t* copied) {
+  if (!s || !demand) return api_error(MOE_ERR_INVALID_ARGUMENT, "store or demand is NULL");
+  if (copy_stream == stream) return api_error(MOE_ERR_INVALID_ARGUMENT, "copy_stream must differ from stream");
+  MOE_RETURN_IF_ERROR(commit(s, stream));
+  std::vector<std::pair<int, const void*>> evict, place;
+  std::vector<std::pair<int, int>> moves;
+  MOE_RETURN_IF_ERROR(choose(s, demand, evict, moves, place));
+  MOE_RETURN_IF_ERROR(push_updates(s, evict, stream));   // (1) on the compute stream
+  hipError_t err = hipEventRecord(s->evicted, stream);
+  if (err == hipSuccess) err = hipStreamWaitEvent(copy_stream, s->evicted, 0);
+  if (err != hipSuccess) return api_error(MOE_ERR_HIP, hipGetErrorString(err));
+  MOE_RETURN_IF_ERROR(copy_in(s, moves, copy_stream));  // (2) on the copy stream, after (1)
+  err = hipEventRecord(s->copied, copy_stream);
+  if (err != hipSuccess) return api_error(MOE_ERR_HIP, hipGetErrorString(err));
+  s->pending_place = place;                 // (3) at the commit
+  s->pending = true;
+  if (copied) *copied = (int32_t)moves.size();
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_store_commit(moe_expert_store_t s, hipStream_t stream) {
+  if (!s) return api_error(MOE_ERR_INVALID_ARGUMENT, "store is NULL");
+  return commit(s, stream);
 }
 
 moe_status_t moe_expert_store_residency(moe_expert_store_t s, int32_t* slot_of) {

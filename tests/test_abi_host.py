@@ -221,4 +221,6 @@ def test_expert_tables_and_store_argument_errors():
     assert L.moe_expert_store_set_expert(None, 0, ok, ok, ok, ok) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_expert_store_weights(None, ctypes.byref(w)) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_expert_store_update(None, ok, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_update_async(None, ok, None, ok, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_store_commit(None, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_expert_store_residency(None, ok) == B.MOE_ERR_INVALID_ARGUMENT

@@ -105,3 +105,53 @@ def test_store_host_reads_and_cache_updates(name):
         assert torch.equal(y3, ref)
     finally:
         store.close()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_store_async_copies_on_a_second_stream(name):
+    """Copies on a copy stream overlap with layers enqueued on the compute stream:
+    before the commit those layers read the incoming experts from host memory,
+    after it from their slots; either way the output is the contiguous-weights
+    output bit for bit."""
+    shape = CASES[name]
+    x, w = G.device_case(shape, seed=5)
+    plain = B.MoELayer(shape, w)
+    ref = plain.forward(x)
+    torch.cuda.synchronize()
+    slots = shape.E_loc // 4
+    store = B.ExpertStore(shape, slots)
+    copy = torch.cuda.Stream()          # default priority, like the compute stream
+    try:
+        store.fill({k: w[k].cpu() for k in ("w1", "b1", "w2", "b2")})
+        L = B.MoELayer(shape, w, store=store)
+        demand = _demand(shape, plain, x)
+        local = demand[shape.e_lo:shape.e_lo + shape.E_loc]
+        want = [e for e in sorted(range(shape.E_loc), key=lambda e: (-local[e], e)) if local[e] > 0][:slots]
+        n = store.update_async(demand, copy)
+        y_before = L.forward(x)          # enqueued while the copies may still run
+        store.commit()
+        y_after = L.forward(x)
+        torch.cuda.synchronize()
+        cached = set(np.nonzero(store.residency() >= 0)[0].tolist())
+        G.say(f"[store async {name}] copied {n} on the copy stream, cached {sorted(cached)}")
+        assert n == len(want) and cached == set(want)
+        assert torch.equal(y_before, ref) and torch.equal(y_after, ref)
+
+        # evictions and new copies; a synchronous update commits the pending one first
+        d2 = np.zeros(shape.E, dtype=np.int32)
+        fresh = [e for e in range(shape.E_loc) if e not in cached][:slots]
+        for e in fresh:
+            d2[shape.e_lo + e] = 10 * int(local.max() + 1)
+        n2 = store.update_async(d2, copy)
+        y_mid = L.forward(x)
+        assert store.update(d2) == 0
+        y_end = L.forward(x)
+        torch.cuda.synchronize()
+        G.say(f"  second update: copied {n2}, cached {sorted(np.nonzero(store.residency() >= 0)[0].tolist())}")
+        assert n2 == len(fresh) and set(np.nonzero(store.residency() >= 0)[0].tolist()) == set(fresh)
+        assert torch.equal(y_mid, ref) and torch.equal(y_end, ref)
+        with pytest.raises(B.MoeError):
+            store.update_async(d2, torch.cuda.current_stream())   # the copy stream must be another stream
+    finally:
+        torch.cuda.synchronize()
+        store.close()
