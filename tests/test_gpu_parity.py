@@ -46,6 +46,10 @@ CASES = {
     "gemm_bm160": W.LayerShape("g160", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
     "gemm_bm160_bf16_share": W.LayerShape("g160b", T=1024, H=512, F=1024, E=8, E_loc=4, e_lo=2, k=2, cf=1.25,
                                           dtype="bf16"),
+    # 160 x 256 tiles with the dense MLP's tiles in the same launches: expert
+    # weights streamed, the MLP's cached (two copies of the K loop)
+    "residual_bm160": W.LayerShape("r160", T=1024, H=512, F=1024, E=4, E_loc=4, k=1, cf=1.25, dtype="f16",
+                                   mlp_type="residual"),
     # edge cases: the maximum expert count (8 logits per lane in the top-k), a
     # ragged token count (gate token blocks of 8), heavy drops (cf = 0.1), one
     # token through a residual layer, and a share of a single local expert
