@@ -140,7 +140,10 @@ __device__ inline float dot_rows(const uint4 (&wv)[RPW][NQ], const typename DT::
 // expert, drops, non-local experts) end after phase 2; their weight loads, if
 // any, read lines the leader reads too.
 #ifndef UP_WAVES
-#define UP_WAVES 8
+#define UP_WAVES 8     // waves of a W1 work-group (W1 kernel 15.9 us against 17.1 with 4 and 16.6 with 16)
+#endif
+#ifndef DOWN_WAVES
+#define DOWN_WAVES 8   // waves of a W2 work-group (W2 kernel 12.6 us against 12.8 with 4 and 12.7 with 2)
 #endif
 #define ROUTE_NTH (UP_WAVES * 64)
 #define ROUTE_MAX_KT 64
@@ -357,14 +360,14 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p
 }
 
 template <typename DT, int MAXM, int NQ, bool FUSE>
-__global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p) {
+__global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodeParams p) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
   constexpr int N = RPW * MAXM;
   constexpr int SH = 6 - ilog2(N);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nchunk = p.H / (4 * RPW);
+  const int nchunk = p.H / (DOWN_WAVES * RPW);
   const int g = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - g * nchunk;
   int seg = 0, r0 = 0, r1 = p.M;
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DecodeParams p) {
     return;
   }
   const long long H = p.H, F = p.F;
-  const int j0 = chunk * 4 * RPW + wave * RPW;
+  const int j0 = chunk * DOWN_WAVES * RPW + wave * RPW;
   const int M = min(r1 - r0, MAXM);
   const int v = lane >> SH;
   const int oi = v / MAXM, om = v - (v / MAXM) * MAXM;
@@ -426,9 +429,9 @@ static hipError_t launch_up_t(const DecodeParams& p, const RouteParams& rp, int 
 template <typename DT, int MAXM, int NQ>
 static hipError_t launch_down_t(const DecodeParams& p, int grid_segs, bool fuse, hipStream_t s, LaunchEv ev) {
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
-  const int grid = grid_segs * (p.H / (4 * RPW));
-  if (fuse) MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, true>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, p);
-  else MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, false>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, p);
+  const int grid = grid_segs * (p.H / (DOWN_WAVES * RPW));
+  if (fuse) MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, true>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s, ev.start, ev.stop, p);
+  else MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, false>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s, ev.start, ev.stop, p);
   return hipGetLastError();
 }
 
