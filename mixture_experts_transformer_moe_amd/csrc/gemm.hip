@@ -172,7 +172,9 @@ __device__ inline bool gemm_tile(const GemmParams& p, int BM, int& seg, int& nt,
 
 // NTH threads (4 or 8 waves, laid out WM x WN over the tile); DEPTH stages of
 // global loads in flight; the launch bound asks for two waves per SIMD when the
-// registers of two stages or of eight waves must fit.
+// registers of two stages or of eight waves must fit. WNT: the expert tiles load
+// their weights non-temporally (the host sets it when every weight tile is read
+// by at most two row tiles).
 template <typename DT, int BM, int BN, int EPI, typename BiasT, int DEPTH, int NTH, bool WNT>
 __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped_gemm_kernel(GemmParams p) {
   using T = typename DT::T;
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 // global -> registers RA/RB for stage KS (all loads of the stage in flight together).
 // The operands are global memory: said so, the loads are global_load (a flat
 // load would also count against lgkmcnt, and every LDS wait would then wait for
-// the stage in flight too). W_: the weights are read once, non-temporally.
+// the stage in flight too). W_: the weights are loaded non-temporally.
 #define GEMM_GLOAD(RA, RB, KS)                                                           \
   {                                                                                      \
     const long long off_ = (long long)(KS) * 128;                                        \
@@ -301,8 +303,9 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #define GEMM_SB __builtin_amdgcn_sched_barrier(0)
 
   // The K loop, with or without non-temporal weight loads. With WNT the expert
-  // tiles stream their weights (each tile read by this work-group only) and the
-  // extra segment's tiles, which all read the same dense weights, keep them cached.
+  // tiles stream their weights (each weight tile is read by one or two row tiles)
+  // and the extra segment's tiles, which all read the same dense weights, keep
+  // them cached: two copies of the loop, one per choice.
   auto k_loop = [&](auto stream_tag) {
     constexpr bool W_ = decltype(stream_tag)::value;
     if constexpr (DEPTH == 1) {
