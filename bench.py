@@ -425,13 +425,41 @@ KERNEL_SOURCES = {
 }
 
 
+def strip_comments(text: str) -> str:
+    """C/C++ source without its comments, blank lines and runs of blanks (line
+    breaks kept for the preprocessor), so that a change to comments or layout
+    does not count as a kernel change."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                     # string or character literal, escapes kept
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (" ".join(line.split()) for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_digest(files) -> str:
-    """sha256 over the named HIP sources: stored counter readings hold only while it matches."""
+    """sha256 over the code of the named HIP sources (comments and whitespace
+    left out): stored counter readings hold only while it matches."""
     import hashlib
     h = hashlib.sha256()
     for f in sorted(files):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + strip_comments(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -22,11 +22,12 @@
 // SIMD). Epilogues: bias + exact GeLU rounded to the I/O dtype (first expert
 // GEMM), or bias in fp32 (second GEMM and gate logits).
 //
-// Tiles come from a device tile list built by the plan kernel from the segment
-// offsets (no host sync): order is segment, then column tile, then m-tile, so
-// the m-tiles that share a weight tile are adjacent; the block index is remapped
-// so adjacent tiles land on the same XCD (work-groups are dealt round-robin over
-// the 8 XCDs) and share its L2.
+// Tiles come from a device tile list built on the device from the kept rows of
+// each segment, by the dispatch kernel that fills the segments or by the plan
+// kernel from segment offsets (no host sync). Order: the extra segment's tiles,
+// then segment, column tile, m-tile, so the m-tiles that share a weight tile are
+// adjacent; the block index is remapped so adjacent tiles land on the same XCD
+// (work-groups are dealt round-robin over the 8 XCDs) and share its L2.
 #include <type_traits>
 
 #include "common.h"
@@ -411,8 +412,8 @@ struct LaunchEv {
 };
 
 // Stages in flight: two for tiles of <= 64 rows (weight streaming, the register
-// budget allows it), one for 128-row tiles (more reuse per byte, and two would
-// cost occupancy).
+// budget allows it) and for the eight-wave 128 x 256 tile; one for 128 x 128 and
+// 160 x 256 tiles (more reuse per byte, and two would cost occupancy).
 template <typename DT, int BM, int BN, int EPI, typename BiasT>
 static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   constexpr int NTH = BN == 256 ? 512 : GEMM_THREADS;
