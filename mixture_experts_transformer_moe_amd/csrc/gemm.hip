@@ -24,10 +24,11 @@
 //
 // Tiles come from a device tile list built on the device from the kept rows of
 // each segment, by the dispatch kernel that fills the segments or by the plan
-// kernel from segment offsets (no host sync). Order: the extra segment's tiles,
-// then segment, column tile, m-tile, so the m-tiles that share a weight tile are
-// adjacent; the block index is remapped so adjacent tiles land on the same XCD
-// (work-groups are dealt round-robin over the 8 XCDs) and share its L2.
+// kernel from segment offsets (no host sync). Order: segment, column tile,
+// m-tile, so the m-tiles that share a weight tile are adjacent, with the extra
+// segment's tiles spread evenly among them; the block index is remapped so
+// adjacent tiles land on the same XCD (work-groups are dealt round-robin over the
+// 8 XCDs) and share its L2.
 #include <type_traits>
 
 #include "common.h"

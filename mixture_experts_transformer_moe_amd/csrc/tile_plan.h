@@ -14,16 +14,16 @@ struct TilePlanArgs {
   int* count;       // count[0] = number of row tiles (the extra segment's included)
   int BM;           // rows per tile
   int n_nt1, n_nt2; // column tiles of the two GEMMs
-  int mt_extra;     // row tiles of the extra segment (id nseg), listed first
+  int mt_extra;     // row tiles of the extra segment (id nseg), spread over the list
 };
 
 // ints of LDS tile_plan_body<NTH> needs
 __host__ __device__ constexpr int tile_plan_lds_ints(int nth) { return 2 * nth + nth / 64 + 2; }
 
-// Thread s < nseg (nseg <= NTH) passes the rows of segment s. Order: the extra
-// segment's tiles first (so they run alongside the expert tiles), then segment
-// by segment, column tile, then row tile, so the row tiles that share a weight
-// tile are adjacent. Every thread of the block must call it.
+// Thread s < nseg (nseg <= NTH) passes the rows of segment s. Expert tiles go
+// segment by segment, column tile, then row tile, so the row tiles that share a
+// weight tile are adjacent; the extra segment's tiles are spread evenly among
+// them. Every thread of the block must call it.
 template <int NTH>
 __device__ inline void tile_plan_body(int rows, int nseg, const TilePlanArgs& a, int* lds) {
   constexpr int NW = NTH / 64;
@@ -61,23 +61,34 @@ __device__ inline void tile_plan_body(int rows, int nseg, const TilePlanArgs& a,
     const int n_nt = g ? a.n_nt2 : a.n_nt1;
     int2* list = g ? a.list2 : a.list1;
     if (!list) continue;
-    const int n_extra = a.mt_extra * n_nt;
-    for (int L = tid; L < n_extra; L += NTH) {
-      const int nt = L / a.mt_extra, mt = L - nt * a.mt_extra;
-      list[L] = make_int2(nseg, (nt << 16) | mt);
-    }
-    for (int L = tid; L < total * n_nt; L += NTH) {
-      const int v = L / n_nt;
+    // The extra segment's n_x tiles are spread evenly over the N entries: the
+    // number of them among entries [0, L] is ceil((L + 1) n_x / N), so entry L
+    // holds one iff that count steps at L. Each stretch of the list, and so each
+    // XCD's share at any moment, mixes the extra segment's tiles (compute-bound
+    // when its weights stay cached) with the expert tiles (weight streaming).
+    const long long n_x = (long long)a.mt_extra * n_nt;
+    const long long N = n_x + (long long)total * n_nt;
+    for (int L = tid; L < N; L += NTH) {
+      const long long cx = n_x ? ((long long)(L + 1) * n_x + N - 1) / N : 0;
+      const long long cp = n_x ? ((long long)L * n_x + N - 1) / N : 0;
+      if (cx > cp) {              // the extra segment's tile cx - 1: column tile major, then row tile
+        const int i = (int)(cx - 1);
+        const int nt = i / a.mt_extra, mt = i - nt * a.mt_extra;
+        list[L] = make_int2(nseg, (nt << 16) | mt);
+        continue;
+      }
+      const int j = (int)(L - cx);   // expert tile j
+      const int v = j / n_nt;
       int lo = 0, hi = nseg;               // largest s with P[s] <= v and P[s+1] > v
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (P[mid] <= v) lo = mid; else hi = mid;
       }
       const int s = lo;
-      const int q = L - P[s] * n_nt;
+      const int q = j - P[s] * n_nt;
       const int cs = C[s];
       const int nt = q / cs, mt = q - (q / cs) * cs;
-      list[n_extra + L] = make_int2(s, (nt << 16) | mt);
+      list[L] = make_int2(s, (nt << 16) | mt);
     }
   }
 }
