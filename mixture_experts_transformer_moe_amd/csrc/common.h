@@ -198,6 +198,9 @@ struct GemmParams {
   // (segments of at most two row tiles), so the launch picks the variant that
   // streams the expert weights with non-temporal loads
   int stream_w;
+  // host only: every operand (A, A2 and each segment's weights) spans less than
+  // 4 GB, so byte offsets from its base fit 32 bits (buffer-load addressing)
+  int off32;
 };
 
 // Expert FFN for segments of at most MAXM rows: each work-group takes one

@@ -95,6 +95,7 @@ struct Plan {
   // gate
   bool gate_mfma;
   bool stream_w;       // expert GEMMs: each weight tile read by <= 2 work-groups (non-temporal weight loads)
+  bool off32;          // GEMM operands each span < 4 GB (32-bit byte offsets)
   int gate_BM, gate_BN;
   int gate_ksplit;     // matrix-core gate: slices of K, each writing fp32 partial logits
   // dispatch
@@ -229,6 +230,10 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   // non-temporal loads (measured faster for both; the dense MLP's tiles in the
   // same launches, read by every token tile, keep their weights cached)
   p.stream_w = !p.exp_decode && seg_rows <= 2 * (int64_t)p.BM;
+  // activations (x, x_disp, h: at most max(T, R_max) rows of max(H, F)) and one
+  // expert's or the MLP's weights (H x F) each below 4 GB
+  p.off32 = std::max<int64_t>(p.T, p.R_max) * std::max(p.H, p.F) * (int64_t)p.esz < ((int64_t)1 << 32) &&
+            (int64_t)p.H * p.F * (int64_t)p.esz < ((int64_t)1 << 32);
   if (p.dense_in_experts) {
     const int64_t mte = (p.T + p.BM - 1) / p.BM;
     if (mte >= 65536) return fail(MOE_ERR_UNSUPPORTED, "too many row tiles");
@@ -453,6 +458,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g1.tile_count = cnt;
   g1.n_ntiles = nt1;
   g1.stream_w = p.stream_w ? 1 : 0;
+  g1.off32 = p.off32 ? 1 : 0;
   if (dense) {   // the residual MLP over all T tokens: h_dense = GeLU(x W1_mlp^T + b1_mlp)
     g1.A2 = x;
     g1.B2 = w->mlp_w1;
@@ -480,6 +486,7 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g2.tile_count = cnt;
   g2.n_ntiles = nt2;
   g2.stream_w = p.stream_w ? 1 : 0;
+  g2.off32 = p.off32 ? 1 : 0;
   if (dense) {   // m = h_dense W2_mlp^T + b2_mlp, fp32
     g2.A2 = wsp<void>(ws, p.o_dh);
     g2.B2 = w->mlp_w2;
@@ -524,6 +531,7 @@ moe_status_t run_dense(const Plan& p, const void* x, const moe_layer_weights_t* 
   g1.bias = w->mlp_b1;
   g1.C = h;
   g1.n_ntiles = p.F / p.dBN1;
+  g1.off32 = p.off32 ? 1 : 0;
   const int mt = (int)((p.T + p.dBM - 1) / p.dBM);
   HIP_TRY(launch_grouped_gemm(p.dtype, EPI_GELU, false, p.dBM, p.dBN1, g1, mt * g1.n_ntiles, s), "dense gemm 1");
   GemmParams g2{};
@@ -536,6 +544,7 @@ moe_status_t run_dense(const Plan& p, const void* x, const moe_layer_weights_t* 
   g2.bias = w->mlp_b2;
   g2.C = out;
   g2.n_ntiles = p.H / p.dBN2;
+  g2.off32 = p.off32 ? 1 : 0;
   HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, false, p.dBM, p.dBN2, g2, mt * g2.n_ntiles, s), "dense gemm 2");
   return MOE_OK;
 }
