@@ -16,13 +16,12 @@
 // padded row pitch leaves every fragment read with bank conflicts. Global loads
 // are full 128-byte lines (8 lanes per row), which HBM serves faster than the
 // 64-byte row pieces the MFMA operand layout would need if loaded directly.
-// Tiles of <= 64 rows (bound by weight bandwidth) and the 128 x 256 tiles keep
-// two stages of loads in flight in a register ping-pong; 128 x 128 and
-// 160 x 256 tiles keep one (two would not fit the registers of two waves per
-// SIMD). The 256-column tiles normally run in grouped_gemm_pp_kernel instead
-// (below): with all eight waves in the same phase of a K step, the LDS reads and
-// the MFMAs of a step ran one after the other, so there the two halves of the
-// work-group run half a step apart. Epilogues: bias + exact GeLU rounded to the I/O dtype (first expert
+// Tiles of <= 64 rows (bound by weight bandwidth) keep two stages of loads in
+// flight in a register ping-pong, 128 x 128 tiles one. The eight-wave 128 x 256
+// and 160 x 256 tiles of long segments and the dense MLP run in
+// grouped_gemm_pp_kernel (below): with all eight waves in the same phase of a K
+// step, the LDS reads and the MFMAs of a step ran one after the other, so there
+// the two halves of the work-group run half a step apart. Epilogues: bias + exact GeLU rounded to the I/O dtype (first expert
 // GEMM), or bias in fp32 (second GEMM and gate logits).
 //
 // Tiles come from a device tile list built on the device from the kept rows of
@@ -591,36 +590,36 @@ struct LaunchEv {
   hipEvent_t start, stop;
 };
 
-// Stages in flight: two for tiles of <= 64 rows (weight streaming, the register
-// budget allows it) and for the eight-wave 128 x 256 tile; one for 128 x 128 and
-// 160 x 256 tiles (more reuse per byte, and two would cost occupancy).
+// Four-wave tiles keep two stages of loads in flight for tiles of <= 64 rows
+// (weight streaming, the register budget allows it), one for 128 x 128 (more
+// reuse per byte, and two would cost occupancy). 256-column tiles run in the
+// eight-wave ping-pong kernel.
 template <typename DT, int BM, int BN, int EPI, typename BiasT>
 static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   constexpr int NTH = BN == 256 ? 512 : GEMM_THREADS;
-  constexpr int DEPTH = (BM <= 64 || (NTH == 512 && BM == 128)) ? 2 : 1;
+  constexpr int DEPTH = BM <= 64 ? 2 : 1;
   const dim3 g(grid, p.ksplit > 1 ? p.ksplit : 1);
-  // eight-wave 256-column tiles: the ping-pong kernel whenever the operands
-  // allow 32-bit offsets (the gate's float-bias tiles are never 256 wide)
-  if constexpr (BN == 256 && !std::is_same<BiasT, float>::value) {
-    if (p.off32) {
-      if (p.stream_w)
-        MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
-      else
-        MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
-      return;
+  if constexpr (BN == 256) {
+    // (launch_grouped_gemm refuses float-bias 256-column tiles and operands
+    // beyond 32-bit offsets before getting here)
+    if constexpr (std::is_same<BiasT, float>::value) return;
+    if (p.stream_w)
+      MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+    else
+      MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+    return;
+  } else {
+    // (float bias: the gate's logits, whose weight tile every token tile reads)
+    if constexpr (!std::is_same<BiasT, float>::value) {
+      if (p.stream_w) {   // expert weights read by one or two row tiles each
+        MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, true>), g, dim3(NTH), 0, s, ev.start,
+                   ev.stop, p);
+        return;
+      }
     }
+    MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, false>), g, dim3(NTH), 0, s, ev.start,
+               ev.stop, p);
   }
-  // (float bias: the gate's logits, whose weight tile every token tile reads;
-  // the two-stage 128 x 256 tile has no registers left for a second loop copy)
-  if constexpr (!std::is_same<BiasT, float>::value && !(BM == 128 && BN == 256)) {
-    if (p.stream_w) {   // expert weights read by one or two row tiles each
-      MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, true>), g, dim3(NTH), 0, s, ev.start,
-                 ev.stop, p);
-      return;
-    }
-  }
-  MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, false>), g, dim3(NTH), 0, s, ev.start, ev.stop,
-             p);
 }
 
 template <typename DT, int BM, int BN>
@@ -666,6 +665,7 @@ static bool launch_bn(int BM, int BN, int epi, bool bias_f32, const GemmParams& 
 hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN, const GemmParams& p, int grid,
                                hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (grid <= 0) return hipSuccess;
+  if (BN == 256 && (bias_f32 || !p.off32)) return hipErrorInvalidValue;   // the ping-pong kernel's limits
   if (p.ksplit > 1) {   // fp32 partial outputs with a float bias only, and whole 128-byte steps per slice
     const long long steps = (long long)p.K * (dtype == DT_F32 ? 4 : 2) / 128;
     if (!bias_f32 || epi != EPI_F32 || p.tiles || steps % p.ksplit != 0 || p.ksplit > 65535)

@@ -95,7 +95,7 @@ struct Plan {
   // gate
   bool gate_mfma;
   bool stream_w;       // expert GEMMs: each weight tile read by <= 2 work-groups (non-temporal weight loads)
-  bool off32;          // GEMM operands each span < 4 GB (32-bit byte offsets)
+  bool off32;          // GEMM operands each span < 4 GB (32-bit byte offsets; 256-column tiles need it)
   int gate_BM, gate_BN;
   int gate_ksplit;     // matrix-core gate: slices of K, each writing fp32 partial logits
   // dispatch
@@ -206,7 +206,12 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   p.BN2 = (p.H % 128 == 0) ? 128 : 64;
   // segments of more than 64 rows: eight-wave 128 x 256 or 160 x 256 tiles
   // (160 when two of them cover a segment that would need three 128-row tiles)
-  const bool big_ok = p.dtype != MOE_DTYPE_F32 && p.F % 256 == 0 && p.H % 256 == 0;
+  // (they address their operands with 32-bit byte offsets: activations x,
+  // x_disp and h, at most max(T, R_max) rows of max(H, F), and one expert's or
+  // the MLP's weights, H x F, must each stay below 4 GB)
+  p.off32 = std::max<int64_t>(p.T, p.R_max) * std::max(p.H, p.F) * (int64_t)p.esz < ((int64_t)1 << 32) &&
+            (int64_t)p.H * p.F * (int64_t)p.esz < ((int64_t)1 << 32);
+  const bool big_ok = p.dtype != MOE_DTYPE_F32 && p.F % 256 == 0 && p.H % 256 == 0 && p.off32;
   if (p.BM == 128 && big_ok) {
     p.BN1 = p.BN2 = 256;
     if (seg_rows > 256 && seg_rows <= 320) p.BM = 160;
@@ -230,10 +235,6 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   // non-temporal loads (measured faster for both; the dense MLP's tiles in the
   // same launches, read by every token tile, keep their weights cached)
   p.stream_w = !p.exp_decode && seg_rows <= 2 * (int64_t)p.BM;
-  // activations (x, x_disp, h: at most max(T, R_max) rows of max(H, F)) and one
-  // expert's or the MLP's weights (H x F) each below 4 GB
-  p.off32 = std::max<int64_t>(p.T, p.R_max) * std::max(p.H, p.F) * (int64_t)p.esz < ((int64_t)1 << 32) &&
-            (int64_t)p.H * p.F * (int64_t)p.esz < ((int64_t)1 << 32);
   if (p.dense_in_experts) {
     const int64_t mte = (p.T + p.BM - 1) / p.BM;
     if (mte >= 65536) return fail(MOE_ERR_UNSUPPORTED, "too many row tiles");

@@ -50,6 +50,11 @@ CASES = {
     # weights streamed, the MLP's cached (two copies of the K loop)
     "residual_bm160": W.LayerShape("r160", T=1024, H=512, F=1024, E=4, E_loc=4, k=1, cf=1.25, dtype="f16",
                                    mlp_type="residual"),
+    # 128 x 256 ping-pong tiles: with the dense MLP's tiles in the same launches,
+    # and in bf16 with top-2 (segments of up to C = 150 rows)
+    "residual_bm128": W.LayerShape("r128", T=1024, H=512, F=1024, E=8, E_loc=8, k=1, cf=1.0, dtype="f16",
+                                   mlp_type="residual"),
+    "gemm_bm128_bf16_k2": W.LayerShape("g128b", T=600, H=256, F=512, E=8, E_loc=8, k=2, cf=1.0, dtype="bf16"),
     # edge cases: the maximum expert count (8 logits per lane in the top-k), a
     # ragged token count (gate token blocks of 8), heavy drops (cf = 0.1), one
     # token through a residual layer, and a share of a single local expert
