@@ -602,12 +602,12 @@ static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) 
   if constexpr (BN == 256) {
     // (launch_grouped_gemm refuses float-bias 256-column tiles and operands
     // beyond 32-bit offsets before getting here)
-    if constexpr (std::is_same<BiasT, float>::value) return;
-    if (p.stream_w)
-      MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
-    else
-      MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
-    return;
+    if constexpr (!std::is_same<BiasT, float>::value) {
+      if (p.stream_w)
+        MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+      else
+        MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+    }
   } else {
     // (float bias: the gate's logits, whose weight tile every token tile reads)
     if constexpr (!std::is_same<BiasT, float>::value) {
