@@ -402,66 +402,73 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 }
 
 
+// s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): wait for vmcnt <= n only, and for lgkmcnt == 0 only
+#define MOE_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+#define MOE_LGKM0 0xC07F
+
 // Eight-wave 256-column tiles (BM = 128 or 160) for long segments and the dense
 // MLP, where the matrix cores set the pace. Ping-pong schedule: waves 0-3 (the
 // tile's upper rows) and waves 4-7 (lower rows) run half a K step apart, so on
-// every SIMD one wave multiplies while the other reads its fragments from LDS,
-// writes its half of the next K step into LDS (from one of two register sets)
-// and issues the loads of the step three ahead into that set. Every wave passes
-// 2 nk + 2 barriers. Measured on the 24B-share expert GEMMs (16 experts,
-// H = 8192, F = 32768, 160 x 256 tiles): 2.95 / 2.75 ms per launch against
-// 3.39 / 3.37 ms with all waves in step.
+// every SIMD one wave multiplies while the other reads its fragments of the next
+// step from LDS. The K steps reach LDS by direct-to-LDS buffer loads (no
+// registers, no LDS store instructions) into three buffers, issued two steps
+// ahead. Every wave passes 2 nk + 2 barriers. Measured on the 24B-share expert
+// GEMMs (16 experts, H = 8192, F = 32768, 160 x 256 tiles): 2.74 / 2.67 ms per
+// launch; 2.91 / 2.74 ms with the steps staged through registers and LDS
+// stores, 3.39 / 3.37 ms with all eight waves in the same phase.
 template <typename DT, int BM, int EPI, typename BiasT, bool WNT>
 __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
   using T = typename DT::T;
   constexpr int BN = 256, WN = 4;
   constexpr int TN = 4, TM = BM / 32;
-  static_assert(TM * 32 == BM, "BM must be a multiple of 32");
-  constexpr int HB = BM / 2;                        // activation rows of one group
-  constexpr int ACH = (HB * 8 + 255) / 256;         // 16-byte activation chunks per thread and K step
-  constexpr int BCH = 4;                            // weight chunks: 128 rows x 8 per group
+  constexpr int HB = BM / 2;
+  constexpr int NCG = 16 + HB / 8;            // 8-row chunks of one group's half of a K step
+  constexpr int NCH = (NCG + 3) / 4;          // chunks per wave (the extras load into a dummy area)
   constexpr int STAGE = (BN + BM) * LDS_ROW;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int DUMMY = 3 * STAGE;
+  __shared__ __attribute__((aligned(16))) char smem[3 * STAGE + (NCH * 4 > NCG ? 1024 : 0)];
 
   int seg, nt, mt, r0, r1;
   if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) return;
   const int m0 = r0 + mt * BM;
   const bool extra = seg == p.nseg;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_n = wave % WN;
-  const int g = wave / WN;                          // group = wave row of the tile
-  const int gt = tid & 255;                         // thread within the group
+  const int g = wave / WN;
 
-  // Buffer loads from work-group-uniform bases with 32-bit byte offsets (the host
-  // guarantees every operand spans less than 4 GB). Group g loads weight rows
-  // [128 g, 128 g + 128) and activation rows [HB g, HB g + HB) of each K step:
-  // chunk i of a thread is row (gt >> 3) + 32 i of its part, 16-byte column
-  // gt & 7, stored in LDS at column c ^ (row & 7). Activation chunks past the
-  // group's rows (the last chunk when HB * 8 is not a multiple of 256) load a
-  // valid duplicate and skip the store.
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(extra ? p.A2 : p.A);
-  unsigned a_off[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int row = g * HB + min((gt >> 3) + 32 * i, HB - 1);
-    int r = m0 + row;
-    if (r >= r1) r = r1 - 1;
-    const long long arow = (p.a_rows && !extra) ? (long long)p.a_rows[r] : (long long)r;
-    a_off[i] = (unsigned)(arow * p.K * (long long)sizeof(T)) + (gt & 7) * 16;
-  }
-  const bool a_last = (gt >> 3) + 32 * (ACH - 1) < HB;
-  const int a_dst = BN * LDS_ROW + (g * HB + (gt >> 3)) * LDS_ROW + (((gt & 7) ^ ((gt >> 3) & 7)) * 16);
   const char* bbase = extra    ? reinterpret_cast<const char*>(p.B2)
                       : p.Bp ? reinterpret_cast<const char*>(p.Bp[seg])
                              : reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
-  const __amdgpu_buffer_rsrc_t b_rsrc =
-      make_rsrc(bbase + ((long long)nt * BN + g * 128) * p.K * (long long)sizeof(T));
-  const int b_lane = (gt >> 3) * p.K * (int)sizeof(T) + (gt & 7) * 16;
-  const int b_step = 32 * p.K * (int)sizeof(T);     // bytes between chunks i and i + 1
-  const int b_dst = (g * 128 + (gt >> 3)) * LDS_ROW + (((gt & 7) ^ ((gt >> 3) & 7)) * 16);
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(bbase + (long long)nt * BN * p.K * (long long)sizeof(T));
+  // chunk i of this wave: c = wave_n + 4 i; c < 16 weight rows 128 g + 8 c, c < NCG
+  // activation rows HB g + 8 (c - 16), else a dummy. A wave's LDS DMA writes
+  // 64 x 16 bytes contiguously: lane l lands in row l / 8 of the chunk, 16-byte
+  // slot l % 8, so it loads column (l % 8) ^ (l / 8) (the XOR swizzle).
+  const int col = ((lane & 7) ^ (lane >> 3)) * 16;
+  unsigned voff[NCH];
+  int ldst[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = wave_n + 4 * i;
+    if (i < 4) {
+      const int row = g * 128 + c * 8 + (lane >> 3);
+      voff[i] = (unsigned)(row * p.K * (int)sizeof(T)) + col;
+      ldst[i] = (g * 128 + c * 8) * LDS_ROW;
+    } else if (c < NCG) {
+      int r = m0 + g * HB + (c - 16) * 8 + (lane >> 3);
+      if (r >= r1) r = r1 - 1;
+      const long long arow = (p.a_rows && !extra) ? (long long)p.a_rows[r] : (long long)r;
+      voff[i] = (unsigned)(arow * p.K * (long long)sizeof(T)) + col;
+      ldst[i] = BN * LDS_ROW + (g * HB + (c - 16) * 8) * LDS_ROW;
+    } else {
+      voff[i] = voff[0];
+      ldst[i] = -1;
+    }
+  }
 
   float4_t acc[TN][TM];
 #pragma unroll
@@ -474,24 +481,19 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
   const int frag_c0 = (((lane >> 4)) ^ (frag_row & 7)) * 16;
   const int frag_c1 = ((4 + (lane >> 4)) ^ (frag_row & 7)) * 16;
 
-#define PP_GLOAD(RA, RB, KS)                                                             \
+#define DM_ISSUE(KS, BUF)                                                                \
   {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < ACH; ++i) RA[i] =                              \
-        __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, (int)a_off[i], (KS) * 128, 0);    \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i) RB[i] =                              \
-        __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane, i * b_step + (KS) * 128,   \
-                                              W_ ? MOE_CPOL_NT : 0);                     \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc,                                   \
+          (__attribute__((address_space(3))) void*)(smem + (BUF) * STAGE + ldst[i]), 16,  \
+          (int)voff[i], (KS) * 128, 0, W_ ? MOE_CPOL_NT : 0);                            \
+    _Pragma("unroll") for (int i = 4; i < NCH; ++i) {                                    \
+      char* dst_ = ldst[i] < 0 ? smem + DUMMY : smem + (BUF) * STAGE + ldst[i];          \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc,                                   \
+          (__attribute__((address_space(3))) void*)dst_, 16, (int)voff[i], (KS) * 128, 0, 0); \
+    }                                                                                    \
   }
-#define PP_LSTORE(RA, RB, BUF)                                                           \
-  {                                                                                      \
-    char* base_ = smem + (BUF) * STAGE;                                                  \
-    _Pragma("unroll") for (int i = 0; i < ACH - 1; ++i)                                  \
-        *reinterpret_cast<u32x4_t*>(base_ + a_dst + i * 32 * LDS_ROW) = RA[i];           \
-    if (a_last) *reinterpret_cast<u32x4_t*>(base_ + a_dst + (ACH - 1) * 32 * LDS_ROW) = RA[ACH - 1]; \
-    _Pragma("unroll") for (int i = 0; i < BCH; ++i)                                      \
-        *reinterpret_cast<u32x4_t*>(base_ + b_dst + i * 32 * LDS_ROW) = RB[i];           \
-  }
-#define PP_FRAGS(BUF)                                                                    \
+#define DM_FRAGS(BUF)                                                                    \
   {                                                                                      \
     const char* sb = smem + (BUF) * STAGE;                                               \
     const char* sa = sb + BN * LDS_ROW;                                                  \
@@ -504,56 +506,61 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
                                                     (kb ? frag_c1 : frag_c0));           \
     }                                                                                    \
   }
-#define PP_MATH                                                                          \
+#define DM_MATH                                                                          \
   {                                                                                      \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
       _Pragma("unroll") for (int i = 0; i < TN; ++i)                                     \
         _Pragma("unroll") for (int j = 0; j < TM; ++j)                                   \
           acc[i][j] = Mfma<DT>::op(fa[kb][i], fb[kb][j], acc[i][j]);                     \
   }
-
-// (nothing may move across a barrier: the schedule is the point)
-#define PP_SB __builtin_amdgcn_sched_barrier(0)
+// A barrier nothing moves across. The waits that make a K step's direct-to-LDS
+// loads visible are explicit (s_waitcnt vmcnt before the barrier); the compiler
+// adds its own vmcnt(0) before the fragment reads while any such load is in
+// flight, which only shortens the lead of the loads to one multiply phase.
+#define DM_BAR                                                                           \
+  {                                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                   \
+    asm volatile("" ::: "memory");                                                       \
+    __builtin_amdgcn_s_barrier();                                                        \
+    asm volatile("" ::: "memory");                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                   \
+  }
 
   auto k_loop = [&](auto stream_tag) {
     constexpr bool W_ = decltype(stream_tag)::value;
-    u32x4_t ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
     uint4 fa[2][TN], fb[2][TM];
-    // K step 0 into LDS buffer 0; steps 1 and 2 into register sets 1 and 0
-    PP_GLOAD(ra0, rb0, 0);
-    PP_LSTORE(ra0, rb0, 0);
-    PP_GLOAD(ra1, rb1, min(1, nk - 1));
-    PP_GLOAD(ra0, rb0, min(2, nk - 1));
-    __syncthreads();
-    // Group 1 passes one extra barrier first and group 0 one extra at the end:
-    // barrier n of a wave then pairs with barrier n of the other group, so group
-    // 0's memory phase of step s + 1 runs beside group 1's multiply phase of step
-    // s, and group 1's memory phase of step s beside group 0's multiply of step s.
-    // At an even step s, register set 1 holds step s + 1 and set 0 step s + 2.
-    if (g == 1) __syncthreads();
-#define PP_HALF(BUF, RA, RB, NEXT)                                                       \
-  {                                                                                      \
-    PP_FRAGS(BUF);                                                                       \
-    if ((NEXT) - 2 < nk) PP_LSTORE(RA, RB, (BUF) ^ 1);                                   \
-    PP_GLOAD(RA, RB, min(NEXT, nk - 1));                                                 \
-    PP_SB;                                                                               \
-    __syncthreads();                                                                     \
-    PP_SB;                                                                               \
-    PP_MATH;                                                                             \
-    PP_SB;                                                                               \
-    __syncthreads();                                                                     \
-    PP_SB;                                                                               \
-  }
-    // (loads past the last step reload it: every load is unconditional, so the
-    // wait for one register set never drains the other)
-    int s = 0;
-    for (; s + 1 < nk; s += 2) {
-      PP_HALF(0, ra1, rb1, s + 3);   // step s; stores step s + 1, loads step s + 3
-      PP_HALF(1, ra0, rb0, s + 4);   // step s + 1; stores step s + 2, loads step s + 4
+    // steps 0 and 1 into LDS buffers 0 and 1; step 0 complete before the barrier
+    DM_ISSUE(0, 0);
+    if (nk > 1) {
+      DM_ISSUE(1, 1);
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT(NCH));
+    } else {
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
     }
-    if (s < nk) PP_HALF(0, ra1, rb1, s + 3);
-#undef PP_HALF
-    if (g == 0) __syncthreads();
+    DM_BAR;
+    // Group 1 passes one extra barrier first and group 0 one extra at the end:
+    // barrier n of a wave then pairs with barrier n of the other group, so one
+    // group's memory phase runs beside the other's multiply phase. Step s lives
+    // in buffer s % 3. Memory phase of step s: fragments of step s, then the DMA
+    // of step s + 2 into buffer (s + 2) % 3 (both groups finished reading step
+    // s - 1 there before the previous barrier), then wait until this wave's DMA
+    // of step s + 1 has landed; a reader of step s + 1 passes a barrier after
+    // both groups' waits.
+    if (g == 1) DM_BAR;
+    for (int s = 0; s < nk; ++s) {
+      DM_FRAGS(s % 3);
+      if (s + 2 < nk) {
+        DM_ISSUE(s + 2, (s + 2) % 3);
+        __builtin_amdgcn_s_waitcnt(MOE_VMCNT(NCH));
+      } else {
+        __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+      }
+      __builtin_amdgcn_s_waitcnt(MOE_LGKM0);
+      DM_BAR;
+      DM_MATH;
+      DM_BAR;
+    }
+    if (g == 0) DM_BAR;
   };
   if constexpr (WNT) {
     if (extra) k_loop(std::false_type{});
@@ -561,11 +568,10 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
   } else {
     k_loop(std::false_type{});
   }
-#undef PP_GLOAD
-#undef PP_LSTORE
-#undef PP_FRAGS
-#undef PP_MATH
-#undef PP_SB
+#undef DM_ISSUE
+#undef DM_FRAGS
+#undef DM_MATH
+#undef DM_BAR
   gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + g * TM * 16, r1, lane);
 }
 
