@@ -22,6 +22,11 @@ CASES = {
     # residual: the dense MLP's tiles ride in the expert GEMM launches
     "residual": W.LayerShape("graph_res", T=256, H=512, F=1024, E=16, E_loc=16, k=1, cf=2.0,
                              mlp_type="residual", dtype="bf16"),
+    # eight-wave ping-pong tiles (direct-to-LDS loads): 160 x 256 expert tiles,
+    # and 128 x 256 tiles with the dense MLP in the same launches
+    "pingpong_160": W.LayerShape("graph_pp160", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
+    "pingpong_128_residual": W.LayerShape("graph_pp128", T=1024, H=512, F=1024, E=8, E_loc=8, k=1, cf=1.0,
+                                          mlp_type="residual", dtype="bf16"),
 }
 
 REPLAYS = 4
