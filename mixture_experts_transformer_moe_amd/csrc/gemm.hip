@@ -8,21 +8,25 @@
 // tile (rows m), so each lane of a 16x16 accumulator holds four consecutive n of
 // one output row: the epilogue stores 4 contiguous values per lane.
 //
-// A work-group computes a BM x BN output tile with 4 waves (8 for the 256-wide
-// tiles of large segments); K advances 128 bytes per stage through
-// double-buffered LDS. In LDS each row keeps its 128 bytes as eight 16-byte
-// columns, column c of row r at position c ^ (r & 7): the row-wise stores and
-// the fragment reads (16 rows at one column) then hit distinct banks, where a
-// padded row pitch leaves every fragment read with bank conflicts. Global loads
-// are full 128-byte lines (8 lanes per row), which HBM serves faster than the
-// 64-byte row pieces the MFMA operand layout would need if loaded directly.
-// Tiles of <= 64 rows (bound by weight bandwidth) keep two stages of loads in
-// flight in a register ping-pong, 128 x 128 tiles one. The eight-wave 128 x 256
-// and 160 x 256 tiles of long segments and the dense MLP run in
-// grouped_gemm_pp_kernel (below): with all eight waves in the same phase of a K
-// step, the LDS reads and the MFMAs of a step ran one after the other, so there
-// the two halves of the work-group run half a step apart. Epilogues: bias + exact GeLU rounded to the I/O dtype (first expert
-// GEMM), or bias in fp32 (second GEMM and gate logits).
+// grouped_gemm_kernel: a work-group computes a BM x BN output tile (BN <= 128)
+// with 4 waves; K advances 128 bytes per stage through double-buffered LDS. In
+// LDS each row keeps its 128 bytes as eight 16-byte columns, column c of row r
+// at position c ^ (r & 7): the row-wise stores and the fragment reads (16 rows
+// at one column) then hit distinct banks, where a padded row pitch leaves every
+// fragment read with bank conflicts. Global loads are full 128-byte lines (8
+// lanes per row), which HBM serves faster than the 64-byte row pieces the MFMA
+// operand layout would need if loaded directly. Tiles of <= 64 rows (bound by
+// weight bandwidth) keep two stages of loads in flight in a register ping-pong,
+// 128 x 128 tiles one.
+//
+// grouped_gemm_pp_kernel: the eight-wave 128 x 256 and 160 x 256 tiles of long
+// segments and the dense MLP. With all eight waves in the same phase of a K
+// step, the LDS reads and the MFMAs of a step ran one after the other; there the
+// two halves of the work-group run half a step apart, and the K steps reach
+// three LDS buffers (same swizzled layout) by direct-to-LDS buffer loads.
+//
+// Epilogues: bias + exact GeLU rounded to the I/O dtype (first expert GEMM), or
+// bias in fp32 (second GEMM and gate logits).
 //
 // Tiles come from a device tile list built on the device from the kept rows of
 // each segment, by the dispatch kernel that fills the segments or by the plan
