@@ -65,6 +65,13 @@ CASES = {
     "residual_t1": W.LayerShape("rt1", T=1, H=512, F=1024, E=8, E_loc=8, k=1, cf=1.0, dtype="f16",
                                 mlp_type="residual"),
     "share_eloc1": W.LayerShape("el1", T=256, H=256, F=512, E=16, E_loc=1, e_lo=5, k=2, cf=1.0, dtype="bf16"),
+    # residual pass-through: a share of 2 of 16 experts (most rows are MLP(x)
+    # alone), and heavy drops (C = 4 of 600 tokens per expert: decode expert
+    # kernels beside the dense MLP's GEMMs)
+    "residual_share_passthrough": W.LayerShape("rsp", T=512, H=256, F=512, E=16, E_loc=2, e_lo=3, k=1, cf=1.0,
+                                               dtype="f16", mlp_type="residual"),
+    "residual_heavy_drop": W.LayerShape("rhd", T=600, H=256, F=512, E=8, E_loc=8, k=1, cf=0.05, dtype="f16",
+                                        mlp_type="residual"),
     # streaming expert kernels fed by the dispatch kernel (batch too large to route in-kernel)
     "decode_unrouted": W.LayerShape("decun", T=512, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
     # the multi-block dispatch writing the GEMM tile lists from its scan block:
