@@ -19,6 +19,9 @@ CASES = {
     "decode": W.LayerShape("store_dec", T=8, H=512, F=1024, E=32, E_loc=32, k=2, cf=1.0, dtype="f16"),
     # grouped GEMM (segments of up to 64 rows), a share of the experts
     "gemm": W.LayerShape("store_gemm", T=512, H=256, F=512, E=16, E_loc=8, e_lo=4, k=2, cf=1.0, dtype="f16"),
+    # eight-wave ping-pong tiles (160 x 256, direct-to-LDS loads) reading each
+    # expert's weights through the pointer tables
+    "gemm_pingpong": W.LayerShape("store_pp", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
 }
 
 
