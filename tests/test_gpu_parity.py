@@ -72,6 +72,10 @@ CASES = {
                                                dtype="f16", mlp_type="residual"),
     "residual_heavy_drop": W.LayerShape("rhd", T=600, H=256, F=512, E=8, E_loc=8, k=1, cf=0.05, dtype="f16",
                                         mlp_type="residual"),
+    # the dense MLP in launches of its own on the ping-pong kernel's single-
+    # segment tiles (128 x 256, no tile list), beside 16-row expert tiles
+    "residual_dense_pingpong": W.LayerShape("rdp", T=4096, H=256, F=4096, E=16, E_loc=16, k=1, cf=0.03125,
+                                            dtype="f16", mlp_type="residual"),
     # streaming expert kernels fed by the dispatch kernel (batch too large to route in-kernel)
     "decode_unrouted": W.LayerShape("decun", T=512, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
     # the multi-block dispatch writing the GEMM tile lists from its scan block:
