@@ -240,8 +240,12 @@ def layer_rows(x_rows, token_slot_rows, w_rows, slot_expert: Sequence[int] | np.
 
     x_rows [n, H]; token_slot_rows [n, k] (slot or -1); w_rows [n, k];
     slot_expert maps a slot to its local expert; expert_weights[e] =
-    (w1, b1, w2, b2) for every local expert the sampled kept slots use.
-    Each expert's FFN runs once on the stack of sampled rows routed to it.
+    (w1, b1, w2, b2) for every local expert the sampled kept slots use, looked
+    up once per expert in increasing order (so a mapping may load them one at a
+    time). Each expert's FFN runs once on the stack of sampled rows routed to it.
+    In residual mode dense_weights = (w1, b1, w2, b2) of the MLP, added once to
+    every row. Pinned against the brute-force dense mixture (every expert on
+    every token, masked by a brute-force dispatch) in the oracle's pin checks.
     """
     x_rows = _f64(x_rows)
     n, H = x_rows.shape

@@ -330,7 +330,71 @@ def check_linearity_and_permutation(O):
     assert np.allclose(rq["y"], nodrop["y"], rtol=1e-12, atol=1e-12)
 
 
+class OnlyExperts(dict):
+    """Expert weights for the experts a sample needs; any other lookup fails (the
+    full-size tests hand layer_rows a mapping that loads one expert at a time)."""
+
+    def __getitem__(self, e):
+        if e not in self.keys():
+            raise KeyError(f"expert {e} was not expected to be needed")
+        return dict.__getitem__(self, e)
+
+
+def check_layer_rows(O):
+    """layer_rows (output rows for a sample of tokens, given their routing) equals
+    the brute-force dense mixture (+ the dense MLP in residual mode) on those rows:
+    top-1 and top-2, drops, residual layers with pass-through rows, local shares,
+    rows sampled out of order and with repeats."""
+    rng = np.random.default_rng(29)
+    #        T   H  F  E  k  cf    e_lo E_loc residual
+    cases = [(24, 5, 7, 4, 1, 1.0, 0, 4, False),
+             (30, 5, 6, 5, 2, 0.75, 0, 5, False),
+             (28, 4, 6, 6, 2, 1.0, 2, 3, False),
+             (20, 5, 8, 4, 1, 0.5, 0, 4, True),
+             (26, 4, 5, 6, 1, 1.0, 1, 2, True)]
+    for T, H, F, E, k, cf, e_lo, E_loc, residual in cases:
+        x, w = tiny_layer(rng, T, H, F, E, E_loc, residual)
+        C = O.capacity(T, E, k, cf)
+        r = O.route(x, w["gate_w"], w["gate_b"], k)
+        d = O.dispatch(r["idx"], E, C, e_lo, E_loc)
+        slot_expert = np.repeat(np.arange(E_loc), np.diff(d["offsets"]))
+        rows = np.concatenate([rng.permutation(T)[: T - 3], [0, 0]])
+        used = {int(slot_expert[s]) for s in d["token_slot"][rows].ravel() if s >= 0}
+        ew = OnlyExperts({e: (w["w1"][e], w["b1"][e], w["w2"][e], w["b2"][e]) for e in used})
+        dense = (w["mlp_w1"], w["mlp_b1"], w["mlp_w2"], w["mlp_b2"]) if residual else None
+        got = O.layer_rows(x[rows], d["token_slot"][rows], r["w"][rows], slot_expert, ew, dense)
+        ref = brute_dense_mixture(None, x, w, E, k, C, e_lo, E_loc)
+        if residual:
+            ref = ref + torch_ffn(x, *dense)
+        assert np.allclose(got, ref[rows], rtol=1e-12, atol=1e-12)
+        # the cases must reach what they are there for
+        kept = d["token_slot"] >= 0
+        assert kept.any()
+        if cf < 1.0 or E_loc < E - e_lo or e_lo > 0:
+            assert (~kept).any()
+
+
+def check_route_override(O):
+    """route with an override (the tests adopt the GPU's legal choice for near-tie
+    tokens) takes the given experts for those tokens, the softmax probabilities at
+    them as weights, and leaves every other token as the plain top-k."""
+    rng = np.random.default_rng(31)
+    x, w = tiny_layer(rng, T=12, H=6, F=4, E=5)
+    plain = O.route(x, w["gate_w"], None, 2)
+    over = {3: np.array([4, 0]), 7: np.array([1, 2])}
+    r = O.route(x, w["gate_w"], None, 2, override=over)
+    z = x @ w["gate_w"].T
+    p = np.exp(z - z.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    for t in range(12):
+        want = over[t] if t in over else brute_topk(z[t:t + 1], 2)[0]
+        assert np.array_equal(r["idx"][t], want)
+        assert np.allclose(r["w"][t], p[t, want], rtol=1e-13, atol=1e-15)
+        if t not in over:
+            assert np.array_equal(r["idx"][t], plain["idx"][t])
+
+
 ALL_CHECKS = [check_softmax, check_gelu, check_topk, check_gate_logits, check_capacity,
               check_dispatch, check_rank_major_priority, check_single_expert_is_dense_ffn,
               check_layer_vs_dense_mixture, check_residual, check_local_shares_sum,
-              check_linearity_and_permutation]
+              check_linearity_and_permutation, check_layer_rows, check_route_override]

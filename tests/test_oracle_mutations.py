@@ -10,7 +10,7 @@ import oracle.moe_oracle as M
 from tests import oracle_pins as P
 
 _orig = {n: getattr(M, n) for n in ("top_k", "dispatch", "gelu", "softmax", "capacity", "combine",
-                                    "ffn", "combine_weights", "gate_logits")}
+                                    "ffn", "combine_weights", "gate_logits", "layer_rows", "route")}
 
 
 def _ties_to_higher(z, k):
@@ -85,7 +85,69 @@ def _gate_no_bias(x, gate_w, gate_b=None):
     return _orig["gate_logits"](x, gate_w, None)
 
 
+def _rows_variant(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights=None, *,
+                  expert_of=None, weight_of=None, dense_per_choice=False):
+    """layer_rows with one step changed (the planted mistakes below)."""
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    n, H = x_rows.shape
+    y = np.zeros((n, H))
+    if dense_weights is not None and not dense_per_choice:
+        y += M.ffn(x_rows, *dense_weights)
+    dense = M.ffn(x_rows, *dense_weights) if dense_weights is not None else None
+    for i in range(n):
+        for j in range(token_slot_rows.shape[1]):
+            s = int(token_slot_rows[i, j])
+            if s < 0:
+                continue
+            e = expert_of(s) if expert_of else int(slot_expert[s])
+            wt = weight_of(i, j) if weight_of else float(w_rows[i, j])
+            y[i] += wt * M.ffn(x_rows[i:i + 1], *expert_weights[e])[0]
+            if dense_per_choice and dense is not None:
+                y[i] += dense[i]
+    return y
+
+
+def _rows_neighbour_expert(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights=None):
+    # the expert of the slot before (wrong at every segment start)
+    return _rows_variant(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights,
+                         expert_of=lambda s: int(slot_expert[max(s - 1, 0)]))
+
+
+def _rows_unweighted(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights=None):
+    return _rows_variant(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights,
+                         weight_of=lambda i, j: 1.0)
+
+
+def _rows_first_choice_weight(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights=None):
+    # every choice weighted by the token's first-choice weight
+    return _rows_variant(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights,
+                         weight_of=lambda i, j: float(w_rows[i, 0]))
+
+
+def _rows_dense_per_choice(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights=None):
+    # the dense MLP added once per kept choice (pass-through rows lose it)
+    return _rows_variant(x_rows, token_slot_rows, w_rows, slot_expert, expert_weights, dense_weights,
+                         dense_per_choice=True)
+
+
+def _route_override_ignored(x, gate_w, gate_b, k, renorm=False, override=None):
+    return _orig["route"](x, gate_w, gate_b, k, renorm, None)
+
+
+def _route_override_keeps_weights(x, gate_w, gate_b, k, renorm=False, override=None):
+    # adopts the experts but keeps the weights of the plain top-k
+    r = _orig["route"](x, gate_w, gate_b, k, renorm, override)
+    plain = _orig["route"](x, gate_w, gate_b, k, renorm, None)
+    return dict(r, w=plain["w"])
+
+
 MUTATIONS = {
+    "rows_neighbour_slot_expert": ("layer_rows", _rows_neighbour_expert),
+    "rows_ignore_weight": ("layer_rows", _rows_unweighted),
+    "rows_first_choice_weight": ("layer_rows", _rows_first_choice_weight),
+    "rows_dense_per_choice": ("layer_rows", _rows_dense_per_choice),
+    "route_override_ignored": ("route", _route_override_ignored),
+    "route_override_stale_weights": ("route", _route_override_keeps_weights),
     "ties_to_higher_index": ("top_k", _ties_to_higher),
     "token_major_priority": ("dispatch", _token_major),
     "keep_pos_le_C": ("dispatch", _keep_le),
