@@ -2,12 +2,15 @@
 memory, experts read straight from pinned host memory, and the expert store's
 device cache after routing-driven updates (with evictions). The kernels do the
 same arithmetic on the same values wherever the weights live, so every
-placement must reproduce the contiguous-weights output bit for bit; the
-residency the store picks is checked against the demand it was given."""
+placement must reproduce the contiguous-weights output bit for bit, and every
+output is also compared with the fp64 oracle's layer on the same inputs (to
+the tolerance of the I/O dtype); the residency the store picks is checked
+against the demand it was given."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from mixture_experts_transformer_moe_amd import binding as B
 from mixture_experts_transformer_moe_amd import workloads as W
 from tests import gpu_helpers as G
@@ -23,6 +26,28 @@ CASES = {
     # expert's weights through the pointer tables
     "gemm_pingpong": W.LayerShape("store_pp", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
 }
+
+
+def _oracle_y(shape, L, x, w):
+    """The oracle's layer output on host copies of the same inputs, the GPU's
+    choice adopted for near-tie tokens (routing must match everywhere else)."""
+    idx = torch.empty((shape.T, shape.k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((shape.T, shape.k), dtype=torch.float32, device="cuda")
+    B.moe_gate(L.desc, x, L.weights["gate_w"], L.weights["gate_b"], idx, tw, None, L.ws)
+    torch.cuda.synchronize()
+    hx, hw = G.host(x), G.host_weights({k: v for k, v in w.items() if v is not None})
+    hw.setdefault("gate_b", None)
+    route = oracle.route(hx, hw["gate_w"], hw["gate_b"], shape.k, shape.renorm)
+    override = G.adopt_near_ties(route, G.host(idx), shape.k)
+    return oracle.layer_forward(hx, hw, E=shape.E, k=shape.k, cf=shape.cf, e_lo=shape.e_lo, E_loc=shape.E_loc,
+                                residual=shape.residual, renorm=shape.renorm, override=override)["y"]
+
+
+def _check(y, ref, y_oracle, shape, what):
+    """Bit-exact against the contiguous-weights output, and within the dtype's
+    tolerance of the oracle."""
+    assert torch.equal(y, ref), what
+    G.assert_close(G.host(y), y_oracle, shape.dtype, what)
 
 
 def _demand(shape, L, x):
@@ -43,7 +68,9 @@ def test_tables_into_device_weights(name):
     shape = CASES[name]
     G.say(f"[tables {name}] E_loc={shape.E_loc} T={shape.T}")
     x, w = G.device_case(shape, seed=2)
-    ref = B.MoELayer(shape, w).forward(x)
+    plain = B.MoELayer(shape, w)
+    ref = plain.forward(x)
+    y_oracle = _oracle_y(shape, plain, x, w)
     tabs = {}
     for key in ("w1", "b1", "w2", "b2"):
         t = w[key]
@@ -55,7 +82,7 @@ def test_tables_into_device_weights(name):
     w2.update(w1=None, b1=None, w2=None, b2=None)
     y = B.MoELayer(shape, w2).forward(x)
     torch.cuda.synchronize()
-    assert torch.equal(y, ref)
+    _check(y, ref, y_oracle, shape, f"{name}: pointer tables into device weights")
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -65,6 +92,7 @@ def test_store_host_reads_and_cache_updates(name):
     plain = B.MoELayer(shape, w)
     ref = plain.forward(x)
     torch.cuda.synchronize()
+    y_oracle = _oracle_y(shape, plain, x, w)
     slots = shape.E_loc // 4
     store = B.ExpertStore(shape, slots)
     try:
@@ -73,7 +101,7 @@ def test_store_host_reads_and_cache_updates(name):
         G.say(f"[store {name}] all experts host-resident")
         y0 = L.forward(x)
         torch.cuda.synchronize()
-        assert torch.equal(y0, ref)
+        _check(y0, ref, y_oracle, shape, f"{name}: all experts host-resident")
         assert np.all(store.residency() == -1)
 
         demand = _demand(shape, plain, x)
@@ -87,7 +115,7 @@ def test_store_host_reads_and_cache_updates(name):
         assert len(set(res[res >= 0].tolist())) == len(cached)          # distinct slots
         y1 = L.forward(x)
         torch.cuda.synchronize()
-        assert torch.equal(y1, ref)
+        _check(y1, ref, y_oracle, shape, f"{name}: after update 1")
 
         # demand moves to experts that are not cached: scores halve, the new ones win
         d2 = np.zeros(shape.E, dtype=np.int32)
@@ -100,12 +128,12 @@ def test_store_host_reads_and_cache_updates(name):
         assert set(np.nonzero(res2 >= 0)[0].tolist()) == set(fresh) and n2 == len(fresh)
         y2 = L.forward(x)
         torch.cuda.synchronize()
-        assert torch.equal(y2, ref)
+        _check(y2, ref, y_oracle, shape, f"{name}: after update 2 (evictions)")
         # the same demand again changes nothing
         assert store.update(d2) == 0
         y3 = L.forward(x)
         torch.cuda.synchronize()
-        assert torch.equal(y3, ref)
+        _check(y3, ref, y_oracle, shape, f"{name}: unchanged update")
     finally:
         store.close()
 
@@ -121,6 +149,7 @@ def test_store_async_copies_on_a_second_stream(name):
     plain = B.MoELayer(shape, w)
     ref = plain.forward(x)
     torch.cuda.synchronize()
+    y_oracle = _oracle_y(shape, plain, x, w)
     slots = shape.E_loc // 4
     store = B.ExpertStore(shape, slots)
     copy = torch.cuda.Stream()          # default priority, like the compute stream
@@ -138,7 +167,8 @@ def test_store_async_copies_on_a_second_stream(name):
         cached = set(np.nonzero(store.residency() >= 0)[0].tolist())
         G.say(f"[store async {name}] copied {n} on the copy stream, cached {sorted(cached)}")
         assert n == len(want) and cached == set(want)
-        assert torch.equal(y_before, ref) and torch.equal(y_after, ref)
+        _check(y_before, ref, y_oracle, shape, f"{name}: async, before the commit")
+        _check(y_after, ref, y_oracle, shape, f"{name}: async, after the commit")
 
         # evictions and new copies; a synchronous update commits the pending one first
         d2 = np.zeros(shape.E, dtype=np.int32)
@@ -152,7 +182,8 @@ def test_store_async_copies_on_a_second_stream(name):
         torch.cuda.synchronize()
         G.say(f"  second update: copied {n2}, cached {sorted(np.nonzero(store.residency() >= 0)[0].tolist())}")
         assert n2 == len(fresh) and set(np.nonzero(store.residency() >= 0)[0].tolist()) == set(fresh)
-        assert torch.equal(y_mid, ref) and torch.equal(y_end, ref)
+        _check(y_mid, ref, y_oracle, shape, f"{name}: second async update, before its commit")
+        _check(y_end, ref, y_oracle, shape, f"{name}: after the synchronous update")
         with pytest.raises(B.MoeError):
             store.update_async(d2, torch.cuda.current_stream())   # the copy stream must be another stream
     finally:
