@@ -27,7 +27,10 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked (host). The caller allocates and
  *     owns every buffer, including the workspace; the library keeps no pointer
- *     past the call, allocates nothing and never synchronises the stream.
+ *     past the call, allocates nothing and never synchronises the stream. The
+ *     one exception is the expert store (moe_expert_store_*), which owns pinned
+ *     host memory and device slots: its set-up calls (create, destroy,
+ *     set_expert) allocate, free and synchronise the device.
  *   - Calls enqueue on `stream` and return at once (stream order). No device data
  *     is read on the host, so a sequence of calls can be captured in a hipGraph.
  *   - Argument errors are found on the host before anything is enqueued; then
@@ -108,9 +111,11 @@ typedef struct {
   const void* const* b2_experts;
 } moe_layer_weights_t;
 
-/* Capacity C = ceil(k * T * cf / E) (host, pure). The pages print no formula;
+/* Capacity C = ceil(k * T * cf / E) (host, pure), computed exactly from the
+ * binary value of cf (saturates at INT64_MAX). The pages print no formula;
  * this is the plainest reading, with the global expert count and no floor.
- * Returns -1 for invalid arguments. */
+ * Returns -1 for invalid arguments: T < 0, E outside [1, 512], k outside
+ * {1, 2}, T * k > 2^30, cf not finite or <= 0 (the descriptor's limits). */
 int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double cf);
 
 /* R_max = min(E_loc * C, k * T): rows of the dispatched buffers (host, pure).
@@ -152,8 +157,14 @@ moe_status_t moe_gate(const moe_layer_desc_t* d, const void* x, const void* gate
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Dispatch (capacity and rank-major drops), atomic-free: per-block counts,
- * column scan, stable in-block ranks. From topk_idx [T, k] int32 (values in
- * [0, E)) writes:
+ * column scan, stable in-block ranks. "[Review] DeepSpeed-MoE", section "What is
+ * MoE?": the gating function sends each token to the expert it selects, so the
+ * tokens of one expert are gathered into that expert's segment before its FFN
+ * runs. The pages give no capacity rule or drop order: the capacity
+ * C = ceil(k T cf / E) and the rank-major priority (all first choices before
+ * any second choice, lower token first) are the plainest readings, and a
+ * dropped assignment contributes nothing. From topk_idx [T, k] int32 (values in
+ * [0, E); others count as no expert) writes:
  *   expert_demand  [E]        assignments per global expert (all, kept or not)
  *   expert_offsets [E_loc+1]  exclusive scan of kept rows per local expert
  *   slot_token     [R_max]    token of each dispatched row, -1 past the last row
@@ -183,12 +194,32 @@ moe_status_t moe_dense_ffn(const moe_layer_desc_t* d, const void* x, const moe_l
 
 /* Combine: y[t] = sum over j with token_slot[t,j] >= 0 of topk_w[t,j] * y_disp[token_slot[t,j]]
  * (+ dense_out[t] when dense_out != NULL), summed in fp32 in choice order and
- * rounded once to dtype. y [T, H] is fully written. */
+ * rounded once to dtype. y [T, H] is fully written; a token with nothing kept
+ * gets 0 (or dense_out[t]). "[Review] DeepSpeed-MoE", section "PR-MoE: Pyramid-
+ * Residual-MoE", part "Phenomenon2": Top2-MoE adds the outputs of the two
+ * experts a token is sent to, and Residual-MoE adds the output of a fixed MLP to
+ * that of the one routed expert; the gate-probability weight w on each expert
+ * term follows the gated mixture of "What is MoE?" (a Switch-Transformer layer).
+ * Arguments: y_disp [R_max, H] fp32 (rows of moe_expert_ffn), token_slot [T, k]
+ * int32 from moe_dispatch (values >= R_max are an error of the caller, never
+ * checked on the device), topk_w [T, k] fp32, dense_out [T, H] fp32 or NULL,
+ * y [T, H] dtype. Errors: INVALID_ARGUMENT for NULL or misaligned pointers. */
 moe_status_t moe_combine(const moe_layer_desc_t* d, const float* y_disp, const int32_t* token_slot,
                          const float* topk_w, const float* dense_out, void* y, hipStream_t stream);
 
 /* The whole layer: x [T, H] dtype -> y [T, H] dtype, using ws of at least
- * moe_workspace_size() bytes. In residual mode the dense MLP runs too. */
+ * moe_workspace_size() bytes. In residual mode the dense MLP runs too. The
+ * layer is the MoE FFN of "[Review] DeepSpeed-MoE", section "What is MoE?" (a
+ * gate picks experts per token, each expert is an FFN, the outputs are mixed by
+ * the gate), in the Top2-MoE and Residual-MoE forms of "Phenomenon2" (section
+ * "PR-MoE: Pyramid-Residual-MoE"); the 'standard' / 'residual' choice is the
+ * mlp_type option of the "DeepSpeed-MoE Inference" wiki page (section on PR-MoE),
+ * and a share of the experts is the expert-parallel placement of that page's
+ * inference set-up. Ownership: x, y, the weights and ws belong to the caller;
+ * ws holds the intermediates (logits, routing, h, y_disp) and may be reused
+ * after the work enqueued on stream has run. Errors: INVALID_ARGUMENT (NULL or
+ * misaligned pointers, bad descriptor), UNSUPPORTED, WORKSPACE_TOO_SMALL, all
+ * found before anything is enqueued; MOE_ERR_HIP when a launch fails. */
 moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const moe_layer_weights_t* w,
                                const void* x, void* y, void* ws, size_t ws_bytes,
                                hipStream_t stream);

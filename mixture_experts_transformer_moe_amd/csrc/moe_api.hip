@@ -51,7 +51,12 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int64_t kMaxAssignments = (int64_t)1 << 30;   // T * k
+
 // Exact ceil(k*T*cf / E) for a finite cf > 0 (cf = mant * 2^e2 exactly).
+// Needs 1 <= E <= 512 and 0 <= T * k <= 2^30 (the callers check both), which
+// keeps every shift below inside 128 bits: A < 2^83 before a left shift of at
+// most 40, and E * 2^s < 2^10 * 2^115.
 int64_t capacity_exact(int64_t T, int32_t E, int32_t k, double cf) {
   if (T == 0) return 0;
   int ex;
@@ -142,7 +147,7 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   if (d->flags & ~MOE_FLAG_RENORM_TOPK) return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flag bits");
   if (d->hidden % 64 || d->ffn % 64) return fail(MOE_ERR_UNSUPPORTED, "hidden and ffn must be multiples of 64");
   if (d->num_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "num_experts > %d", kMaxExperts);
-  if (d->num_tokens * (int64_t)d->top_k > (int64_t)(1 << 30))
+  if (d->num_tokens * (int64_t)d->top_k > kMaxAssignments)
     return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k > 2^30");
   if (d->ffn > (1 << 20) || d->hidden > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "hidden / ffn > 2^20");
 
@@ -582,6 +587,8 @@ extern "C" {
 
 int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double cf) {
   if (T < 0 || E < 1 || k < 1 || !(cf > 0.0) || !isfinite(cf)) return -1;
+  // the limits a layer descriptor has (beyond them the exact arithmetic would overflow)
+  if (E > kMaxExperts || k > 2 || T > kMaxAssignments / k) return -1;
   return capacity_exact(T, E, k, cf);
 }
 

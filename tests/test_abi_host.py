@@ -41,6 +41,17 @@ def test_capacity_table_and_oracle_agree():
     assert B.moe_capacity(10, 4, 1, 0.0) == -1
     assert B.moe_capacity(10, 4, 1, float("nan")) == -1
     assert B.moe_capacity(10, 0, 1, 1.0) == -1
+    # beyond the descriptor's limits the exact arithmetic would overflow: refused
+    assert B.moe_capacity(2 ** 30, 1000, 1, 1e-17) == -1          # E > 512
+    assert B.moe_capacity(1000, 2 ** 30, 1, 1e-17) == -1          # E > 512
+    assert B.moe_capacity(2 ** 40, 1, 2, 2.0 ** 90) == -1         # T * k > 2^30 (shifts past 128 bits)
+    assert B.moe_capacity(2 ** 40, 4, 2, 2.0 ** 90) == -1         # T * k > 2^30
+    assert B.moe_capacity(8, 4, 3, 1.0) == -1                     # k not in {1, 2}
+    # at the limits: exact, or saturated at INT64_MAX
+    assert B.moe_capacity(2 ** 29, 512, 2, 1e-17) == 1
+    assert B.moe_capacity(2 ** 29, 2, 2, 2.0 ** 90) == 2 ** 63 - 1
+    assert B.moe_capacity(2 ** 30, 512, 1, 2.0 ** -40) == 1
+    assert B.moe_capacity(2 ** 30, 3, 1, 1.5) == oracle.capacity(2 ** 30, 3, 1, 1.5)
 
 
 def test_max_rows_of_benchmark_layers():
