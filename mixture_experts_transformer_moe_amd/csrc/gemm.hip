@@ -469,7 +469,11 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
       voff[i] = (unsigned)(arow * p.K * (long long)sizeof(T)) + col;
       ldst[i] = BN * LDS_ROW + (g * HB + (c - 16) * 8) * LDS_ROW;
     } else {
-      voff[i] = voff[0];
+      // a spare chunk (160-row tiles: 28 chunk slots for 26 chunks) repeats this
+      // wave's first activation chunk (i == 4, always a real one, its row clamped
+      // into the segment), since DM_ISSUE reads chunks i >= 4 through the
+      // activation descriptor; its data lands in the dummy LDS area
+      voff[i] = voff[4];
       ldst[i] = -1;
     }
   }

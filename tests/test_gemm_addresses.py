@@ -1,0 +1,77 @@
+"""Address bounds of the ping-pong grouped GEMM's direct-to-LDS loads (CPU only).
+
+The eight-wave 128 x 256 / 160 x 256 tiles load each K step through two buffer
+descriptors without range checks: the weight descriptor starts at the tile's
+first weight row, the activation descriptor at row 0 of the activation matrix.
+This replays the kernel's per-lane offset formulas for every wave, lane and
+chunk of a tile and checks that every 16-byte read of every K step stays inside
+its matrix, for the tile shapes the layer plan picks, including tiles taller
+than the whole batch (the 160-row tile of a 150-token top-2 layer)."""
+import pytest
+
+from mixture_experts_transformer_moe_amd import binding as B
+
+
+def pp_offsets(BM, K, esz, m0, r1, a_rows=None):
+    """(descriptor, byte offset) of every chunk load of every lane, as the kernel
+    computes them: chunks i < 4 are weight rows, the rest activation rows
+    (clamped into the segment), spare chunk slots repeat chunk 4."""
+    HB = BM // 2
+    NCG = 16 + HB // 8
+    NCH = (NCG + 3) // 4
+    out = []
+    for wave in range(8):
+        wave_n, g = wave % 4, wave // 4
+        for lane in range(64):
+            col = ((lane & 7) ^ (lane >> 3)) * 16
+            voff = []
+            for i in range(NCH):
+                c = wave_n + 4 * i
+                if i < 4:
+                    row = g * 128 + c * 8 + (lane >> 3)
+                    voff.append(("w", row * K * esz + col))
+                elif c < NCG:
+                    r = min(m0 + g * HB + (c - 16) * 8 + (lane >> 3), r1 - 1)
+                    arow = a_rows[r] if a_rows is not None else r
+                    voff.append(("a", arow * K * esz + col))
+                else:
+                    voff.append(("a", voff[4][1]))
+            out.extend(voff)
+    return out
+
+
+def check_tile(BM, K, esz, m0, r1, a_total_rows, a_rows=None):
+    nk = K * esz // 128
+    last = (nk - 1) * 128 + 16          # the last step's 16 bytes past the base offset
+    for kind, off in pp_offsets(BM, K, esz, m0, r1, a_rows):
+        assert off >= 0
+        if kind == "w":
+            assert off + last <= 256 * K * esz, (BM, kind, off)
+        else:
+            assert off + last <= a_total_rows * K * esz, (BM, kind, off, a_total_rows)
+
+
+@pytest.mark.parametrize("BM", [128, 160])
+def test_expert_tiles_stay_inside_operands(BM):
+    # first GEMM: A = x [T, H] read through slot_token; second GEMM: A = h [R_max, F]
+    for T, H, seg in [(150, 256, 150), (1024, 512, 300), (20, 512, 17), (129, 256, 129)]:
+        for r0 in (0, T - seg):
+            r1 = r0 + seg
+            a_rows = [min(r, T - 1) for r in range(r1)]         # any token index < T
+            for mt in range((seg + BM - 1) // BM):
+                check_tile(BM, H, 2, r0 + mt * BM, r1, T, a_rows)
+                check_tile(BM, H, 2, r0 + mt * BM, r1, r1)       # h rows
+
+
+@pytest.mark.parametrize("BM", [128, 160])
+def test_dense_mlp_tiles_stay_inside_x(BM):
+    for T in (1, 100, 150, 160, 300):
+        for mt in range((T + BM - 1) // BM):
+            check_tile(BM, 512, 2, mt * BM, T, T)
+
+
+def test_plan_picks_160_rows_for_short_batches():
+    """The layer plan does send a 150-token top-2 layer to 160-row tiles, so the
+    bound above is what keeps its loads inside x."""
+    plan = B.moe_layer_plan(B.make_desc(150, 256, 512, 2, 2, 2.0, "f16"))
+    assert plan["tile"] == (160, 256, 256)

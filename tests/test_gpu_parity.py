@@ -55,6 +55,10 @@ CASES = {
     "residual_bm128": W.LayerShape("r128", T=1024, H=512, F=1024, E=8, E_loc=8, k=1, cf=1.0, dtype="f16",
                                    mlp_type="residual"),
     "gemm_bm128_bf16_k2": W.LayerShape("g128b", T=600, H=256, F=512, E=8, E_loc=8, k=2, cf=1.0, dtype="bf16"),
+    # 160 x 256 tiles over a batch of fewer than 160 tokens (C = 300, segments of
+    # 150 rows): every activation load of the first GEMM, spare chunks included,
+    # must stay inside x's 150 rows
+    "gemm_bm160_t150": W.LayerShape("g160t", T=150, H=256, F=512, E=2, E_loc=2, k=2, cf=2.0, dtype="f16"),
     # edge cases: the maximum expert count (8 logits per lane in the top-k), a
     # ragged token count (gate token blocks of 8), heavy drops (cf = 0.1), one
     # token through a residual layer, and a share of a single local expert
