@@ -82,6 +82,71 @@ def layer_flops(shape, rows: int) -> int:
     return f
 
 
+# the grouped-GEMM workloads measured beside the decode headline, in one process
+PREFILL_CONFIGS = ["prefill_1p3b_moe128", "prmoe_residual", "share_24b_moe128"]
+RIDGE = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop per byte where the two roofs meet
+
+
+def graded_bound(shape, n_active: float, rows: float) -> str:
+    """The roof a layer is graded against: the matrix cores once its arithmetic
+    intensity (algorithmic flops per algorithmic byte) reaches half the ridge,
+    else HBM bandwidth."""
+    return "mfma" if layer_flops(shape, rows) / layer_bytes(shape, n_active) >= RIDGE / 2 else "hbm"
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi, by the device's PCI address)
+    from a background thread while the timed passes run."""
+
+    def __init__(self, period_s: float = 0.02):
+        import threading
+        self.mhz, self.err, self.period = [], None, period_s
+        self._stop = threading.Event()
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            pr = torch.cuda.get_device_properties(0)
+            bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+            self._smi = amdsmi
+            self._handle = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
+            self._read()
+        except Exception as e:          # monitoring only: report why it is missing
+            self.err = f"{type(e).__name__}: {e}"[:160]
+            self._handle = None
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self) -> float:
+        info = self._smi.amdsmi_get_clock_info(self._handle, self._smi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.mhz.append(self._read())
+            except Exception as e:
+                self.err = f"{type(e).__name__}: {e}"[:160]
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._handle is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._handle is not None:
+            self._thread.join(timeout=2)
+
+    def summary(self) -> dict:
+        if not self.mhz:
+            return {"mhz_median": None, "samples": 0, "source": "amdsmi gfx clock", "error": self.err}
+        v = np.array(self.mhz)
+        return {"mhz_median": float(np.median(v)), "mhz_min": float(v.min()), "mhz_max": float(v.max()),
+                "samples": int(v.size), "source": "amdsmi gfx clock, sampled every 20 ms during the timed passes"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,7 +160,11 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="independent weight sets rotated per step")
     ap.add_argument("--batches", type=int, default=64, help="token batches rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--config-cpu-seconds", type=float, default=6.0,
+                    help="budget of the oracle CPU baseline of each extra grouped-GEMM workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only --workload (no extra grouped-GEMM workloads in the same run)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the pass that times the expert kernels with launch-recorded events")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -112,21 +181,97 @@ def main():
 
     if args.stack:
         return run_stack(args)
+    torch.cuda.set_device(0)
     shape = W.WORKLOADS[args.workload]
+    clock = ClockSampler()
+    with clock:
+        head = run_layer(shape, args, cpu_budget=0.0 if args.no_cpu_baseline else args.cpu_seconds,
+                         store_slots=args.store_slots)
+    torch.cuda.empty_cache()
+
+    configs = {}
+    if not args.no_configs and args.workload == "decode_350m_moe128" and args.store_slots is None:
+        for name in PREFILL_CONFIGS:
+            with ClockSampler() as ck:
+                r = run_layer(W.WORKLOADS[name], args, cpu_budget=0.0 if args.no_cpu_baseline
+                              else args.config_cpu_seconds)
+            configs[name] = config_entry(r, ck.summary())
+            torch.cuda.empty_cache()
+            print(f"[bench] {name}: {r['ms_per_step'] * 1e3:.1f} us/step, graded {configs[name]['graded']}",
+                  file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic",
+        "plan": head["plan"],
+        "config": head["config"],
+        "roofline": head["roofline"],
+        **({"store": head["store"]} if head.get("store") else {}),
+        "layer": head["layer"],
+        "step_us": head["step_us"],
+        "clock": clock.summary(),
+    }
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    if configs:
+        out["configs"] = configs
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.float16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    print(json.dumps(out), flush=True)
+
+
+def config_entry(r: dict, clock: dict) -> dict:
+    """The compact record of one extra workload in the headline line."""
+    lay = r["layer"]
+    bound = lay["graded_bound"]
+    frac = lay["mfma_frac"] if bound == "mfma" else lay["hbm_frac"]
+    e = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"], "step_us": r["step_us"],
+         "f_hbm": lay["hbm_frac"], "f_mfma": lay["mfma_frac"],
+         "graded": {"bound": bound, "frac": frac,
+                    "target": 0.5 if bound == "mfma" else 0.7},
+         "config": r["config"], "plan": r["plan"], "roofline": r["roofline"],
+         "layer": {k: lay[k] for k in ("algorithmic_bytes", "algorithmic_flops", "mean_active_experts",
+                                       "mean_rows", "phase_us")},
+         "clock": clock}
+    if "cpu_baseline" in r:
+        e["cpu_baseline"] = r["cpu_baseline"]
+    return e
+
+
+def run_layer(shape, args, *, cpu_budget: float, store_slots=None) -> dict:
+    """Times moe_layer_forward on one workload: the K timed steps (value), the
+    same steps with an event pair around each (p10 / p50 / p90), the same
+    steps each after a 1 GiB write that evicts the caches (cold), then the
+    phase-event and kernel-event passes that time the dominant kernel."""
     n_layers = args.layers if args.layers else (4 if shape.T <= 64 else 1)
     n_batches = args.batches if shape.T <= 64 else min(args.batches, 2)
     dev = "cuda"
-    torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
     # ---- inputs, resident in HBM before any timing
     weights = [W.make_weights(shape, seed=s, device=dev) for s in range(n_layers)]
     xs = [W.make_x(shape, seed=1000 + b, device=dev) for b in range(n_batches)]
     stores = []
-    if args.store_slots is not None:
+    if store_slots is not None:
         # experts in pinned host memory, a device cache of store_slots experts per layer
         for w in weights:
-            st_ = B.ExpertStore(shape, args.store_slots)
+            st_ = B.ExpertStore(shape, store_slots)
             st_.fill({k: w[k].cpu() for k in ("w1", "b1", "w2", "b2")})
             stores.append(st_)
     layers = [B.MoELayer(shape, w, store=stores[i] if stores else None) for i, w in enumerate(weights)]
@@ -169,17 +314,21 @@ def main():
                 for li in range(n_layers) for bi in range(n_batches)]
         host_experts = np.mean([np.sum(res[li][active_sets[li, bi]] < 0)
                                 for li in range(n_layers) for bi in range(n_batches)])
-        store_info = {"slots": args.store_slots, "experts_copied": int(sum(copied)),
+        store_info = {"slots": store_slots, "experts_copied": int(sum(copied)),
                       "resident_hit_rate": round(float(np.mean(hits)), 4),
                       "host_read_experts_per_step": round(float(host_experts), 3),
                       "host_read_bytes_per_step": int(host_experts * expert_unit_bytes(shape))}
     del idx, tw, demand, offsets, slot_token, token_slot
     torch.cuda.synchronize()
 
-    def step(i):
-        layers[i % n_layers].forward(xs[(i // n_layers) % n_batches], y, stream)
+    def lb(i):
+        return i % n_layers, (i // n_layers) % n_batches
 
-    print(f"[bench] inputs ready, routing stats taken ({n_layers} weight sets x {n_batches} batches)",
+    def step(i, events=None):
+        li, bi = lb(i)
+        layers[li].forward(xs[bi], y, stream, events=events)
+
+    print(f"[bench] {shape.name}: inputs ready, routing stats taken ({n_layers} weight sets x {n_batches} batches)",
           file=sys.stderr, flush=True)
     # ---- warmup, then exactly K timed steps
     for i in range(args.warmup):
@@ -198,11 +347,39 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     tokens_per_s = shape.T * args.steps / (ms_total / 1e3)
+    print(f"[bench] {shape.name}: timed pass done: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
-    print(f"[bench] timed pass done: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
-    # ---- second pass over the same K steps with per-phase HIP events (same stream):
-    # gate, dispatch, the two expert kernels (W1 kernel "up", W2 kernel "down"), combine
     hip = _Hip()
+    # ---- per-step distribution: an event pair around each step (same steps, same stream)
+    pe0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    pe1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.warmup):
+        step(i)
+    for i in range(args.steps):
+        pe0[i].record(stream)
+        step(i)
+        pe1[i].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in zip(pe0, pe1)]) * 1e3
+    # ---- cold: before each step write 1 GiB (evicts the L2s and the 256 MB Infinity Cache)
+    flush = torch.empty(1 << 29, dtype=torch.float16, device=dev)
+    for i in range(args.steps):
+        flush.fill_(float(i & 7))
+        pe0[i].record(stream)
+        step(i)
+        pe1[i].record(stream)
+    torch.cuda.synchronize()
+    cold = np.array([a.elapsed_time(b) for a, b in zip(pe0, pe1)]) * 1e3
+    del flush
+    step_us = {"p10": round(float(np.percentile(per_step, 10)), 2), "p50": round(float(np.median(per_step)), 2),
+               "p90": round(float(np.percentile(per_step, 90)), 2),
+               "cold_p50": round(float(np.median(cold)), 2),
+               "note": "event pair around each of the K steps (warm: the steps rotate weight sets and batches as in "
+                       "the timed pass); cold: each step after a 1 GiB write that evicts the L2s and the "
+                       "Infinity Cache"}
+
+    # ---- phase events (same stream): gate, dispatch, the two expert kernels
+    # (W1 kernel "up", W2 kernel "down"), combine
     names = ["gate", "dispatch", "up", "down", "combine"]
     pairs = [("gate_begin", "gate_end"), ("dispatch_begin", "dispatch_end"), ("ffn_begin", "ffn_split"),
              ("ffn_split", "ffn_end"), ("combine_begin", "combine_end")]
@@ -211,28 +388,29 @@ def main():
     for i in range(args.warmup):
         step(i)
     for i in range(args.steps):
-        pe = B.PhaseEvents(**{f: e.value for f, e in evs[i].items()})
-        layers[i % n_layers].forward(xs[(i // n_layers) % n_batches], y, stream, events=pe)
+        step(i, B.PhaseEvents(**{f: e.value for f, e in evs[i].items()}))
     torch.cuda.synchronize()
     phase_ms = {n: 0.0 for n in names}
     s_w = 4 if shape.dtype == "f32" else 2
     HF = shape.H * shape.F
     win_bytes = {"up": 0, "down": 0}
     win_flops = {"up": 0, "down": 0}
+    units = 0
     for i in range(args.steps):
         for n, (a, b) in zip(names, pairs):
             phase_ms[n] += hip.elapsed_ms(evs[i][a], evs[i][b])
-        li, bi = i % n_layers, (i // n_layers) % n_batches
+        li, bi = lb(i)
         na, nr = int(n_active[li, bi]), int(rows[li, bi])
+        units += na
         win_bytes["up"] += na * (HF + shape.F) * s_w
         win_bytes["down"] += na * (HF + shape.H) * s_w + ((2 * HF + shape.F + shape.H) * s_w if shape.residual else 0)
-        win_flops["up"] += 2 * HF * nr
-        win_flops["down"] += 2 * HF * nr + (4 * HF * shape.T if shape.residual else 0)
+        win_flops["up"] += 2 * HF * nr + (2 * HF * shape.T if shape.residual else 0)
+        win_flops["down"] += 2 * HF * nr + (2 * HF * shape.T if shape.residual else 0)
     for d in evs:
         for e in d.values():
             hip.destroy(e)
-    # ---- third pass: the expert kernels timed by their own dispatch (start / end
-    # timestamps of the launch itself, no queue packets between kernels)
+    # ---- the expert kernels timed by their own dispatch (start / end timestamps
+    # of the launch itself, no queue packets between kernels)
     plan = B.moe_layer_plan(desc)
     kern_ms = {"up": phase_ms["up"], "down": phase_ms["down"]}
     kernel_events = not args.no_kernel_events
@@ -241,8 +419,7 @@ def main():
         for i in range(args.warmup):
             step(i)
         for i in range(args.steps):
-            pe = B.PhaseEvents(**{f: e.value for f, e in kev[i].items()})
-            layers[i % n_layers].forward(xs[(i // n_layers) % n_batches], y, stream, events=pe)
+            step(i, B.PhaseEvents(**{f: e.value for f, e in kev[i].items()}))
         torch.cuda.synchronize()
         kern_ms = {"up": 0.0, "down": 0.0}
         for i in range(args.steps):
@@ -251,20 +428,30 @@ def main():
         for d in kev:
             for e in d.values():
                 hip.destroy(e)
-    # with the dense MLP (residual mode) the W2 window also holds the MLP kernels:
-    # there the phase-event window is the measured unit
+    dense_inside = bool(plan["dense_in_expert_kernels"])
     if shape.residual:
-        kern_ms["down"] = phase_ms["down"]
+        if dense_inside:
+            # the MLP's first product runs in the W1 launch, its second in the W2 launch
+            win_bytes["up"] += (HF + shape.F) * s_w * args.steps
+            win_bytes["down"] -= (HF + shape.F) * s_w * args.steps
+        else:
+            # the MLP's two launches follow the W2 kernel: the phase window is the unit
+            kern_ms["down"] = phase_ms["down"]
+            win_flops["up"] -= 2 * HF * shape.T * args.steps
+            win_flops["down"] += 2 * HF * shape.T * args.steps
     kern = max(("up", "down"), key=lambda n: kern_ms[n])
     k_s = kern_ms[kern] / 1e3
     achieved_gbs = win_bytes[kern] / k_s / 1e9
     achieved_tflops = win_flops[kern] / k_s / 1e12
     mean_active = float(n_active.mean())
     mean_rows = float(rows.mean())
-    lay_b = layer_bytes(shape, mean_active)
-    lay_f = layer_flops(shape, mean_rows)
-    hbm_bound = achieved_gbs / HBM_PEAK_GBS >= achieved_tflops / MFMA_F16_PEAK_TFLOPS
-    if hbm_bound:
+    # the layer's algorithmic work over the timed steps (the pairs they visit)
+    steps_active = np.mean([n_active[lb(i)] for i in range(args.steps)])
+    steps_rows = np.mean([rows[lb(i)] for i in range(args.steps)])
+    lay_b = layer_bytes(shape, steps_active)
+    lay_f = layer_flops(shape, steps_rows)
+    bound = graded_bound(shape, steps_active, steps_rows)
+    if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
     else:
@@ -272,64 +459,61 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
     if kern == "up":
         unit_b = (HF + shape.F) * s_w
+        unit_f = 2 * HF
         kname = "expert W1 kernel (h = GeLU(x W1^T + b1))"
     else:
         unit_b = (HF + shape.H) * s_w
-        kname = "expert W2 kernel (y = h W2^T + b2)" + (" + dense MLP" if shape.residual else "")
+        unit_f = 2 * HF
+        kname = "expert W2 kernel (y = h W2^T + b2)"
+    if shape.residual:
+        kname += " + dense MLP " + ("tiles in the same launch" if dense_inside else "launches after it")
     roof.update(kernel=kname,
                 avg_launch_us=round(kern_ms[kern] * 1e3 / args.steps, 2),
-                timing=("kernel dispatch start/end events" if kernel_events and not (shape.residual and kern == "down")
+                timing=("kernel dispatch start/end events" if kernel_events and (dense_inside or not shape.residual
+                                                                               or kern == "up")
                         else "phase events around the kernel window"),
-                bytes_per_launch=int(win_bytes[kern] / args.steps), unit="GB/s" if hbm_bound else "TFLOP/s",
-                unit_bytes=unit_b, units_per_launch=round(mean_active, 3),
+                bytes_per_launch=int(win_bytes[kern] / args.steps),
+                flops_per_launch=int(win_flops[kern] / args.steps),
+                unit_bytes=unit_b, unit_flops_per_row=unit_f,
+                units_per_launch=round(units / args.steps, 3),
+                rows_per_launch=round(float(steps_rows), 2),
+                frac_hbm=round(achieved_gbs / HBM_PEAK_GBS, 4),
+                frac_mfma=round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                 kernels_us={n: round(v * 1e3 / args.steps, 2) for n, v in kern_ms.items()},
                 ffn_phase={"us": round((kern_ms["up"] + kern_ms["down"]) * 1e3 / args.steps, 2),
                            "GB/s": round((win_bytes["up"] + win_bytes["down"]) /
                                          ((kern_ms["up"] + kern_ms["down"]) / 1e3) / 1e9, 1)})
     roof["traffic"] = measured_traffic(shape.name, kern)
 
-    if args.copy_probe_mb:
-        n = args.copy_probe_mb * (1 << 20) // 2
-        src = torch.empty(n, dtype=torch.float16, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    out = {
-        "metric": METRIC,
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    res = {
+        "tokens_per_s": round(tokens_per_s, 1),
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": shape.dtype,
-        "data": "synthetic",
+        "step_us": step_us,
         "plan": plan,
         "config": {"workload": shape.name, "tokens": shape.T, "hidden": shape.H, "ffn": shape.F,
-                   "experts": shape.E, "local_experts": shape.E_loc, "top_k": shape.k,
-                   "capacity_factor": shape.cf, "mlp_type": shape.mlp_type, "weight_sets": n_layers,
-                   "token_batches": n_batches, "parallelism": "one GPU"},
+                   "experts": shape.E, "local_experts": shape.E_loc, "first_local_expert": shape.e_lo,
+                   "top_k": shape.k, "capacity_factor": shape.cf, "mlp_type": shape.mlp_type,
+                   "zipf_s": shape.zipf_s, "weight_sets": n_layers, "token_batches": n_batches,
+                   "parallelism": "one GPU"},
         "roofline": roof,
-        **({"store": store_info} if store_info else {}),
         "layer": {"hbm_frac": round(lay_b / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "mfma_frac": round(lay_f / (ms_per_step / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                  "graded_bound": bound,
                   "algorithmic_bytes": int(lay_b), "algorithmic_flops": int(lay_f),
-                  "mean_active_experts": round(mean_active, 3), "mean_rows": round(mean_rows, 2),
+                  "mean_active_experts": round(float(steps_active), 3), "mean_rows": round(float(steps_rows), 2),
+                  "all_pairs_mean_active_experts": round(mean_active, 3),
                   "phase_us": {n: round(v * 1e3 / args.steps, 2) for n, v in phase_ms.items()},
                   "wall_s": round(wall, 3)},
     }
-    print("[bench] event passes done", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, weights[0], xs, args.cpu_seconds)
+    if store_info:
+        res["store"] = store_info
+    print(f"[bench] {shape.name}: event passes done", file=sys.stderr, flush=True)
+    if cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(shape, weights[0], xs, cpu_budget)
     for st_ in stores:
         st_.close()
-    print(json.dumps(out), flush=True)
+    del layers, weights, xs, y, ws
+    return res
 
 
 def run_stack(args):
@@ -480,29 +664,83 @@ def measured_traffic(workload: str, kern: str):
             "total_bytes": k["read_bytes"] + k["write_bytes"], "unit": "bytes per launch"}
 
 
-def cpu_baseline(shape, w, xs, budget_s: float) -> dict:
-    """The fp64 oracle on the same inputs (host copies), over as many token
-    batches as fit in the time budget; tokens/s scaled from that sample."""
-    import oracle
+def _threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
     except Exception:
-        threads = 1
-    hw = {k: W.to_host_f64_ready(v) for k, v in w.items()}
-    hxs = [W.to_host_f64_ready(x) for x in xs]
-    n = 0
+        return 1
+
+
+def cpu_baseline(shape, w, xs, budget_s: float) -> dict:
+    """The fp64 oracle on host copies of the same inputs, timed on the host cores.
+
+    Decode-sized batches: whole oracle layer forwards over the rotating token
+    batches until the budget is spent. Larger batches (one forward can take
+    tens of seconds): one batch, with the oracle's own steps timed one by one:
+    gate, softmax, top-k and dispatch of every token, then the expert FFNs in
+    local-expert order until the budget is spent (the remaining experts'
+    time scaled by their dispatched rows: an expert's FFN cost is linear in its
+    rows), the dense MLP in residual mode, and the combine."""
+    import oracle
+    threads = _threads()
+    if shape.T <= 64:
+        hw = {k: W.to_host_f64_ready(v) for k, v in w.items()}
+        hxs = [W.to_host_f64_ready(x) for x in xs]
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.layer_forward(hxs[n % len(hxs)], hw, E=shape.E, k=shape.k, cf=shape.cf, e_lo=shape.e_lo,
+                                 E_loc=shape.E_loc, residual=shape.residual, renorm=shape.renorm)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= 10000:
+                break
+        return {"value": round(shape.T * n / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{n} layer forwards of {shape.T} tokens (weight set 0, rotating token batches), "
+                          f"{el:.1f} s, numpy float64",
+                "cpu_model": _cpu_model()}
+    hx = W.to_host_f64_ready(xs[0])
+    gw = W.to_host_f64_ready(w["gate_w"])
+    gb = W.to_host_f64_ready(w["gate_b"])
     t0 = time.perf_counter()
-    while True:
-        oracle.layer_forward(hxs[n % len(hxs)], hw, E=shape.E, k=shape.k, cf=shape.cf, e_lo=shape.e_lo,
-                             E_loc=shape.E_loc, residual=shape.residual, renorm=shape.renorm)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 10000:
+    r = oracle.route(hx, gw, gb, shape.k, shape.renorm)
+    C = oracle.capacity(shape.T, shape.E, shape.k, shape.cf)
+    d = oracle.dispatch(r["idx"], shape.E, C, shape.e_lo, shape.E_loc)
+    t_route = time.perf_counter() - t0
+    off = d["offsets"]
+    active = [e for e in range(shape.E_loc) if off[e + 1] > off[e]]
+    t_ffn, rows_done, n_done = 0.0, 0, 0
+    y_disp = np.zeros((d["R"], shape.H))
+    for e in active:
+        a, b = int(off[e]), int(off[e + 1])
+        ew = [W.to_host_f64_ready(w[n][e]) for n in ("w1", "b1", "w2", "b2")]   # host copy, not timed
+        t1 = time.perf_counter()
+        y_disp[a:b] = oracle.ffn(hx[d["slot_token"][a:b]], *ew)
+        t_ffn += time.perf_counter() - t1
+        rows_done += b - a
+        n_done += 1
+        del ew
+        if t_route + t_ffn >= budget_s:
             break
-    return {"value": round(shape.T * n / el, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} layer forwards of {shape.T} tokens (weight set 0, rotating token batches), "
-                      f"{el:.1f} s, numpy float64",
+    t_ffn_all = t_ffn * (d["R"] / max(rows_done, 1))
+    t_dense = 0.0
+    dense = None
+    if shape.residual:
+        mw = [W.to_host_f64_ready(w[n]) for n in ("mlp_w1", "mlp_b1", "mlp_w2", "mlp_b2")]
+        t1 = time.perf_counter()
+        dense = oracle.ffn(hx, *mw)
+        t_dense = time.perf_counter() - t1
+    t1 = time.perf_counter()
+    oracle.combine(y_disp, d["token_slot"], r["w"], shape.T, shape.H, dense)
+    t_comb = time.perf_counter() - t1
+    total = t_route + t_ffn_all + t_dense + t_comb
+    return {"value": round(shape.T / total, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one batch of {shape.T} tokens: gate, softmax, top-k and dispatch of all tokens "
+                      f"({t_route:.1f} s); FFNs of {n_done} of {len(active)} active experts timed "
+                      f"({rows_done} of {d['R']} rows, {t_ffn:.1f} s) and scaled by rows to {t_ffn_all:.1f} s"
+                      + (f"; dense MLP over all tokens {t_dense:.1f} s" if shape.residual else "")
+                      + f"; combine {t_comb:.1f} s; numpy float64",
             "cpu_model": _cpu_model()}
 
 

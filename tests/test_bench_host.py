@@ -36,3 +36,30 @@ def test_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
     f.write_text("__global__ void k(float* p) { p[0] = 2.f; }\n")
     assert b.kernel_source_digest(["k.hip"]) != d0
 
+
+
+def test_graded_bound_follows_arithmetic_intensity():
+    """Decode and the two HBM-bound prefill layers are graded on HBM bandwidth,
+    the 24B share (intensity near the ridge) on the matrix cores."""
+    b = _bench()
+    from mixture_experts_transformer_moe_amd import workloads as W
+    S = W.WORKLOADS
+    assert b.graded_bound(S["decode_350m_moe128"], 7.8, 7.8) == "hbm"
+    assert b.graded_bound(S["prefill_1p3b_moe128"], 32, 483) == "hbm"
+    assert b.graded_bound(S["prmoe_residual"], 64, 2048) == "hbm"
+    assert b.graded_bound(S["share_24b_moe128"], 16, 4628) == "mfma"
+
+
+def test_cpu_baseline_on_a_prefill_shaped_batch():
+    """The sampled oracle baseline of a large batch (routing of every token, some
+    experts timed, the rest scaled by rows) runs on host tensors and says what it
+    sampled."""
+    b = _bench()
+    from mixture_experts_transformer_moe_amd import workloads as W
+    for shape in (W.REDUCED["prefill_reduced"].with_(T=256, H=128, F=256),
+                  W.REDUCED["residual_reduced"].with_(T=128, H=64, F=128)):
+        w = W.make_weights(shape, 0)
+        xs = [W.make_x(shape, 1000)]
+        r = b.cpu_baseline(shape, w, xs, 0.05)
+        assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+        assert "active experts" in r["sample"] and "rows" in r["sample"]
