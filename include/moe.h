@@ -224,6 +224,25 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const moe_layer_weight
                                const void* x, void* y, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
+/* Bytes of the device scratch array that moe_layer_forward_noalloc uses in
+ * place of a workspace (one copy per GPU, held until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, serving loops, harnesses
+ * that forbid allocation): the intermediates live in the library's own device
+ * scratch array of MOE_NOALLOC_SCRATCH_BYTES per GPU (enough for every layer
+ * whose moe_workspace_size is at most that, e.g. 8- to 4096-token batches of
+ * the 350M / 1.3B +MoE-128 shapes), so the call allocates nothing. The caller
+ * still owns x, y and the weights. Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (on different streams, or from several
+ * threads without ordering) race and give wrong results; calls ordered on one
+ * stream are fine. Errors: as moe_layer_forward, and WORKSPACE_TOO_SMALL when
+ * the layer needs more than MOE_NOALLOC_SCRATCH_BYTES (found before anything
+ * is enqueued). */
+moe_status_t moe_layer_forward_noalloc(const moe_layer_desc_t* d, const moe_layer_weights_t* w,
+                                       const void* x, void* y, hipStream_t stream);
+
 /* Optional timing hook for moe_layer_forward_ex. Any non-NULL event of the first
  * group is recorded on the stream right before / after the phase (gate, dispatch,
  * expert FFN, combine); ffn_split is recorded between the two expert kernels (after

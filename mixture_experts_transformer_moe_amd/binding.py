@@ -24,7 +24,7 @@ MOE_FLAG_RENORM_TOPK = 1
 
 EXPORTED = ["moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_layer_plan", "moe_gate", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_ffn", "moe_combine", "moe_layer_forward",
-            "moe_layer_forward_ex", "moe_status_str", "moe_last_error",
+            "moe_layer_forward_ex", "moe_layer_forward_noalloc", "moe_status_str", "moe_last_error",
             "moe_expert_store_create", "moe_expert_store_destroy", "moe_expert_store_set_expert",
             "moe_expert_store_weights", "moe_expert_store_update", "moe_expert_store_update_async",
             "moe_expert_store_commit", "moe_expert_store_residency"]
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [D, P, P, P, P, P, P]
         L.moe_layer_forward.restype = st
         L.moe_layer_forward.argtypes = [D, W, P, P, P, sz, P]
+        L.moe_layer_forward_noalloc.restype = st
+        L.moe_layer_forward_noalloc.argtypes = [D, W, P, P, P]
         L.moe_layer_forward_ex.restype = st
         L.moe_layer_forward_ex.argtypes = [D, W, P, P, P, sz, P, ctypes.POINTER(PhaseEvents)]
         L.moe_expert_store_create.restype = st
@@ -251,6 +253,14 @@ def moe_layer_forward(desc, weights: LayerWeights, x, y, ws, stream=None):
     p, n = _ws(ws)
     _check(lib().moe_layer_forward(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), _ptr(y), p, n,
                                    _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_layer_forward_noalloc(desc, weights: LayerWeights, x, y, stream=None):
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), _ptr(y),
+                                           _stream(stream)))
 
 
 def moe_layer_forward_ex(desc, weights: LayerWeights, x, y, ws, stream=None, events: Optional[PhaseEvents] = None):

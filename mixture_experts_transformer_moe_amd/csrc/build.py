@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["moe_api.hip", "gate.hip", "dispatch.hip", "gemm.hip", "decode_ffn.hip", "combine.hip", "expert_store.hip"]
+SOURCES = ["moe_api.hip", "gate.hip", "dispatch.hip", "gemm.hip", "decode_ffn.hip", "combine.hip", "expert_store.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
