@@ -96,12 +96,14 @@ def graded_bound(shape, n_active: float, rows: float) -> str:
 
 class ClockSampler:
     """Samples the GPU's graphics clock (amdsmi, by the device's PCI address)
-    from a background thread while the timed passes run."""
+    from a background thread, keeping the samples taken while `active` is set
+    (the timed passes)."""
 
-    def __init__(self, period_s: float = 0.02):
+    def __init__(self, period_s: float = 0.01):
         import threading
         self.mhz, self.err, self.period = [], None, period_s
         self._stop = threading.Event()
+        self.active = threading.Event()
         self._handle = None
         try:
             import amdsmi
@@ -123,7 +125,8 @@ class ClockSampler:
     def _run(self):
         while not self._stop.is_set():
             try:
-                self.mhz.append(self._read())
+                if self.active.is_set():
+                    self.mhz.append(self._read())
             except Exception as e:
                 self.err = f"{type(e).__name__}: {e}"[:160]
                 return
@@ -144,7 +147,8 @@ class ClockSampler:
             return {"mhz_median": None, "samples": 0, "source": "amdsmi gfx clock", "error": self.err}
         v = np.array(self.mhz)
         return {"mhz_median": float(np.median(v)), "mhz_min": float(v.min()), "mhz_max": float(v.max()),
-                "samples": int(v.size), "source": "amdsmi gfx clock, sampled every 20 ms during the timed passes"}
+                "samples": int(v.size), "source": "amdsmi gfx clock, sampled every 10 ms during the timed and "
+                                                  "per-step passes"}
 
 
 def main():
@@ -186,7 +190,7 @@ def main():
     clock = ClockSampler()
     with clock:
         head = run_layer(shape, args, cpu_budget=0.0 if args.no_cpu_baseline else args.cpu_seconds,
-                         store_slots=args.store_slots)
+                         store_slots=args.store_slots, clock=clock)
     torch.cuda.empty_cache()
 
     configs = {}
@@ -194,7 +198,7 @@ def main():
         for name in PREFILL_CONFIGS:
             with ClockSampler() as ck:
                 r = run_layer(W.WORKLOADS[name], args, cpu_budget=0.0 if args.no_cpu_baseline
-                              else args.config_cpu_seconds)
+                              else args.config_cpu_seconds, clock=ck)
             configs[name] = config_entry(r, ck.summary())
             torch.cuda.empty_cache()
             print(f"[bench] {name}: {r['ms_per_step'] * 1e3:.1f} us/step, graded {configs[name]['graded']}",
@@ -243,7 +247,7 @@ def config_entry(r: dict, clock: dict) -> dict:
     frac = lay["mfma_frac"] if bound == "mfma" else lay["hbm_frac"]
     e = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"], "step_us": r["step_us"],
          "f_hbm": lay["hbm_frac"], "f_mfma": lay["mfma_frac"],
-         "graded": {"bound": bound, "frac": frac,
+         "graded": {"bound": bound, "frac": float(frac),
                     "target": 0.5 if bound == "mfma" else 0.7},
          "config": r["config"], "plan": r["plan"], "roofline": r["roofline"],
          "layer": {k: lay[k] for k in ("algorithmic_bytes", "algorithmic_flops", "mean_active_experts",
@@ -254,7 +258,7 @@ def config_entry(r: dict, clock: dict) -> dict:
     return e
 
 
-def run_layer(shape, args, *, cpu_budget: float, store_slots=None) -> dict:
+def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -> dict:
     """Times moe_layer_forward on one workload: the K timed steps (value), the
     same steps with an event pair around each (p10 / p50 / p90), the same
     steps each after a 1 GiB write that evicts the caches (cold), then the
@@ -337,6 +341,8 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None) -> dict:
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if clock:
+        clock.active.set()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
@@ -360,6 +366,8 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None) -> dict:
         step(i)
         pe1[i].record(stream)
     torch.cuda.synchronize()
+    if clock:
+        clock.active.clear()
     per_step = np.array([a.elapsed_time(b) for a, b in zip(pe0, pe1)]) * 1e3
     # ---- cold: before each step write 1 GiB (evicts the L2s and the 256 MB Infinity Cache)
     flush = torch.empty(1 << 29, dtype=torch.float16, device=dev)
