@@ -124,13 +124,19 @@ class ClockSampler:
 
     def _run(self):
         while not self._stop.is_set():
-            try:
-                if self.active.is_set():
-                    self.mhz.append(self._read())
-            except Exception as e:
-                self.err = f"{type(e).__name__}: {e}"[:160]
-                return
-            self._stop.wait(self.period)
+            if self.active.wait(0.05):
+                self.sample_now()
+                self._stop.wait(self.period)
+
+    def sample_now(self):
+        """One reading (also called from the timing loop itself, for passes
+        shorter than the thread's period)."""
+        if self._handle is None:
+            return
+        try:
+            self.mhz.append(self._read())
+        except Exception as e:
+            self.err = f"{type(e).__name__}: {e}"[:160]
 
     def __enter__(self):
         if self._handle is not None:
@@ -169,6 +175,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="time only --workload (no extra grouped-GEMM workloads in the same run)")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="decode path: both expert products in one launch (MOE_FLAG_DECODE_ONE_LAUNCH)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the pass that times the expert kernels with launch-recorded events")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -187,6 +195,8 @@ def main():
         return run_stack(args)
     torch.cuda.set_device(0)
     shape = W.WORKLOADS[args.workload]
+    if args.one_launch:
+        shape = shape.with_(one_launch=True)
     clock = ClockSampler()
     with clock:
         head = run_layer(shape, args, cpu_budget=0.0 if args.no_cpu_baseline else args.cpu_seconds,
@@ -194,7 +204,14 @@ def main():
     torch.cuda.empty_cache()
 
     configs = {}
-    if not args.no_configs and args.workload == "decode_350m_moe128" and args.store_slots is None:
+    if not args.no_configs and args.workload == "decode_350m_moe128" and args.store_slots is None \
+            and not args.one_launch:
+        # the same decode workload with both expert products in one launch
+        with ClockSampler() as ck:
+            r = run_layer(shape.with_(one_launch=True), args, cpu_budget=0.0, clock=ck)
+        configs["decode_350m_moe128_one_launch"] = config_entry(r, ck.summary())
+        torch.cuda.empty_cache()
+        print(f"[bench] decode, one launch: {r['ms_per_step'] * 1e3:.2f} us/step", file=sys.stderr, flush=True)
         for name in PREFILL_CONFIGS:
             with ClockSampler() as ck:
                 r = run_layer(W.WORKLOADS[name], args, cpu_budget=0.0 if args.no_cpu_baseline
@@ -347,6 +364,8 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -
     ev0.record(stream)
     for i in range(args.steps):
         step(i)
+        if clock and i % 8 == 7:
+            clock.sample_now()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -420,10 +439,15 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -
     # ---- the expert kernels timed by their own dispatch (start / end timestamps
     # of the launch itself, no queue packets between kernels)
     plan = B.moe_layer_plan(desc)
+    one_launch = bool(plan["experts_one_launch"])
+    if one_launch:   # both products in the W1 window's one launch
+        win_bytes = {"up": win_bytes["up"] + win_bytes["down"], "down": 0}
+        win_flops = {"up": win_flops["up"] + win_flops["down"], "down": 0}
     kern_ms = {"up": phase_ms["up"], "down": phase_ms["down"]}
     kernel_events = not args.no_kernel_events
     if kernel_events:
-        kev = [{f: hip.event() for f in ("up_start", "up_stop", "down_start", "down_stop")} for _ in range(args.steps)]
+        kf = ("up_start", "up_stop") if one_launch else ("up_start", "up_stop", "down_start", "down_stop")
+        kev = [{f: hip.event() for f in kf} for _ in range(args.steps)]
         for i in range(args.warmup):
             step(i)
         for i in range(args.steps):
@@ -432,7 +456,8 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -
         kern_ms = {"up": 0.0, "down": 0.0}
         for i in range(args.steps):
             kern_ms["up"] += hip.elapsed_ms(kev[i]["up_start"], kev[i]["up_stop"])
-            kern_ms["down"] += hip.elapsed_ms(kev[i]["down_start"], kev[i]["down_stop"])
+            if not one_launch:
+                kern_ms["down"] += hip.elapsed_ms(kev[i]["down_start"], kev[i]["down_stop"])
         for d in kev:
             for e in d.values():
                 hip.destroy(e)
@@ -465,7 +490,12 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -
     else:
         roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    if kern == "up":
+    if kern == "up" and one_launch:
+        unit_b = (2 * HF + shape.F + shape.H) * s_w
+        unit_f = 4 * HF
+        kname = ("expert FFN kernel (routing, h = GeLU(x W1^T + b1), y = h W2^T + b2"
+                 + (" and the top-1 combine" if plan["combine_in_expert_kernel"] else "") + " in one launch)")
+    elif kern == "up":
         unit_b = (HF + shape.F) * s_w
         unit_f = 2 * HF
         kname = "expert W1 kernel (h = GeLU(x W1^T + b1))"
@@ -498,7 +528,8 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -
         "ms_per_step": round(ms_per_step, 5),
         "step_us": step_us,
         "plan": plan,
-        "config": {"workload": shape.name, "tokens": shape.T, "hidden": shape.H, "ffn": shape.F,
+        "config": {"workload": shape.name + ("_one_launch" if shape.one_launch else ""), "tokens": shape.T,
+                   "hidden": shape.H, "ffn": shape.F,
                    "experts": shape.E, "local_experts": shape.E_loc, "first_local_expert": shape.e_lo,
                    "top_k": shape.k, "capacity_factor": shape.cf, "mlp_type": shape.mlp_type,
                    "zipf_s": shape.zipf_s, "weight_sets": n_layers, "token_batches": n_batches,

@@ -70,6 +70,14 @@ typedef enum { MOE_MLP_STANDARD = 0, MOE_MLP_RESIDUAL = 1 } moe_mlp_type_t;
 /* Divide the k combine weights of a token by their sum (before drops). Off by
  * default: the combine weight is the raw softmax probability of the expert. */
 #define MOE_FLAG_RENORM_TOPK 1u
+/* Decode-sized batches (the path where the first expert kernel routes the batch
+ * itself): run both expert products in one launch, the hidden rows handed from
+ * the W1 work-groups to the W2 work-groups through memory inside the launch
+ * ("DeepSpeed Inference" review, proposed-method section: fusing the operators
+ * of small batches into few kernels). Same results bit for bit; ignored where
+ * moe_layer_plan does not report experts_one_launch. Off by default: on MI355X
+ * the two-launch form measures as fast or faster. */
+#define MOE_FLAG_DECODE_ONE_LAUNCH 2u
 
 typedef struct {
   int64_t num_tokens;          /* T >= 0 */
@@ -144,6 +152,7 @@ typedef struct {
   int32_t launches;                   /* kernel launches of one moe_layer_forward */
   int32_t tile_rows;                  /* grouped GEMM: rows per tile (0 on the streaming path) */
   int32_t tile_cols_w1, tile_cols_w2; /* grouped GEMM: columns per tile of the two products */
+  int32_t experts_one_launch;         /* 1: both expert products (and the routing) in one launch */
 } moe_layer_plan_t;
 moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out /* host */);
 

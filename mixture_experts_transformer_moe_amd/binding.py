@@ -21,6 +21,7 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 MOE_DTYPE_F32, MOE_DTYPE_F16, MOE_DTYPE_BF16 = 0, 1, 2
 MOE_MLP_STANDARD, MOE_MLP_RESIDUAL = 0, 1
 MOE_FLAG_RENORM_TOPK = 1
+MOE_FLAG_DECODE_ONE_LAUNCH = 2
 
 EXPORTED = ["moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_layer_plan", "moe_gate", "moe_dispatch",
             "moe_expert_ffn", "moe_dense_ffn", "moe_combine", "moe_layer_forward",
@@ -58,7 +59,8 @@ class LayerPlan(ctypes.Structure):
                 ("gate_path", ctypes.c_int), ("expert_path", ctypes.c_int),
                 ("dispatch_in_expert_kernel", ctypes.c_int32), ("combine_in_expert_kernel", ctypes.c_int32),
                 ("dense_in_expert_kernels", ctypes.c_int32), ("launches", ctypes.c_int32),
-                ("tile_rows", ctypes.c_int32), ("tile_cols_w1", ctypes.c_int32), ("tile_cols_w2", ctypes.c_int32)]
+                ("tile_rows", ctypes.c_int32), ("tile_cols_w1", ctypes.c_int32), ("tile_cols_w2", ctypes.c_int32),
+                ("experts_one_launch", ctypes.c_int32)]
 
 
 EXPERT_PATHS = {0: "grouped_gemm", 1: "stream"}
@@ -162,7 +164,8 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream))
 
 
-def make_desc(T, H, F, E, k, cf, dtype, *, e_lo=0, E_loc=None, residual=False, renorm=False) -> LayerDesc:
+def make_desc(T, H, F, E, k, cf, dtype, *, e_lo=0, E_loc=None, residual=False, renorm=False,
+              one_launch=False) -> LayerDesc:
     if isinstance(dtype, torch.dtype):
         code = _DTYPE_CODE[dtype]
     elif isinstance(dtype, str):
@@ -172,13 +175,15 @@ def make_desc(T, H, F, E, k, cf, dtype, *, e_lo=0, E_loc=None, residual=False, r
     return LayerDesc(num_tokens=T, hidden=H, ffn=F, num_experts=E, first_local_expert=e_lo,
                      num_local_experts=(E - e_lo) if E_loc is None else E_loc, top_k=k,
                      capacity_factor=float(cf), mlp_type=MOE_MLP_RESIDUAL if residual else MOE_MLP_STANDARD,
-                     dtype=code, flags=MOE_FLAG_RENORM_TOPK if renorm else 0)
+                     dtype=code, flags=(MOE_FLAG_RENORM_TOPK if renorm else 0) |
+                     (MOE_FLAG_DECODE_ONE_LAUNCH if one_launch else 0))
 
 
 def desc_from_shape(shape, T: Optional[int] = None) -> LayerDesc:
     """Descriptor for a workloads.LayerShape (optionally with another token count)."""
     return make_desc(shape.T if T is None else T, shape.H, shape.F, shape.E, shape.k, shape.cf, shape.dtype,
-                     e_lo=shape.e_lo, E_loc=shape.E_loc, residual=shape.residual, renorm=shape.renorm)
+                     e_lo=shape.e_lo, E_loc=shape.E_loc, residual=shape.residual, renorm=shape.renorm,
+                     one_launch=shape.one_launch)
 
 
 def make_weights(w: dict) -> LayerWeights:
@@ -211,6 +216,7 @@ def moe_layer_plan(desc: LayerDesc) -> dict:
                 dispatch_in_expert_kernel=bool(pl.dispatch_in_expert_kernel),
                 combine_in_expert_kernel=bool(pl.combine_in_expert_kernel),
                 dense_in_expert_kernels=bool(pl.dense_in_expert_kernels), launches=pl.launches,
+                experts_one_launch=bool(pl.experts_one_launch),
                 tile=(pl.tile_rows, pl.tile_cols_w1, pl.tile_cols_w2))
 
 

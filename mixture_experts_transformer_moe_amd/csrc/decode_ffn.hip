@@ -15,6 +15,8 @@
 // segment's activation rows and a single multi-value wave reduction sums the
 // RPW x MAXM dot products. Work-group g x c takes the g-th non-empty segment
 // (found by each wave on its own from the offsets) and the c-th block of rows.
+#include <algorithm>
+
 #include "common.h"
 #include "dispatch_common.h"
 #include "kernels.h"
@@ -175,13 +177,15 @@ __device__ inline RouteLds route_lds(const RouteParams& rp, int* sh) {
 }
 
 // Phase 1. Returns the local expert of assignment a, or -1 (a >= kT, non-local).
-__device__ inline int route_phase1(const RouteParams& rp, const RouteLds& L, int a) {
+// all_weights: every work-group computes the softmax weights (in LDS), not only
+// work-group 0.
+__device__ inline int route_phase1(const RouteParams& rp, const RouteLds& L, int a, bool all_weights = false) {
   constexpr int NW = ROUTE_NTH / 64;
   const int E = rp.E, T = rp.T, k = rp.k;
   const int w = threadIdx.x >> 6;
   const bool writer = blockIdx.x == 0;
   for (int t = w; t < T; t += NW) {
-    if (writer) {
+    if (writer || all_weights) {
       int sel[2];
       wave_softmax_topk(rp.z + (long long)t * E, E, k, rp.renorm != 0, nullptr, L.lidx + t * k, L.lw + t * k, sel);
     } else {
@@ -409,6 +413,254 @@ __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodePara
   }
 }
 
+// ---------------------------------------------------------------- one launch for both products
+// Cache-policy bit of buffer loads and stores (gfx950): sc1 = agent scope. Such
+// a store is written through the L2 of its XCD and such a load is served past
+// it, so data handed from one work-group to another inside a launch never meets
+// a stale line in another XCD's L2 (the same bit the compiler sets on relaxed
+// agent-scope atomic loads and stores).
+#define MOE_CPOL_AGENT 16
+// Give-up time of the wait for another work-group's hidden rows: 50 ms of the
+// 100 MHz real-time counter (a launch normally waits a few microseconds).
+#define MOE_WAIT_TICKS 5000000ull
+
+__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
+// Dot products of the wave's rows with MAXM activation rows held in LDS (row m
+// at act + m * ld); same accumulation order as dot_rows.
+template <typename DT, int MAXM, int NQ, int RPW>
+__device__ inline float dot_rows_lds(const uint4 (&wv)[RPW][NQ],
+                                     const __attribute__((address_space(3))) typename DT::T* act, int ld) {
+  const int lane = threadIdx.x & 63;
+  float acc[RPW * MAXM];
+#pragma unroll
+  for (int i = 0; i < RPW * MAXM; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      const uint4 av = __builtin_bit_cast(uint4, *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+                                                     act + m * ld + (lane + 64 * q) * DT::VEC));
+      float af[DT::VEC];
+      unpack16<DT>(av, af);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) acc[i * MAXM + m] = dot16f<DT>(wv[i][q], af, acc[i * MAXM + m]);
+    }
+  }
+  return wave_reduce_multi<RPW * MAXM>(acc);
+}
+
+// A 16-bit element still holding the fill pattern 0xFFFF (a NaN the layer never
+// produces: NaN inputs are outside the layer's contract) has not been written.
+__device__ inline bool has_unwritten(const uint4& v) {
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+  bool u = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u |= (w[i] & 0xFFFFu) == 0xFFFFu || (w[i] >> 16) == 0xFFFFu;
+  return u;
+}
+
+// The expert FFN of a decode-sized batch in one launch. Work-group (g, c)
+// routes the batch (as decode_up_kernel), streams chunk c of W1 of the expert
+// whose segment assignment g leads and stores its part of h (agent-scope
+// stores, written through to memory), then streams chunk c of W2 without
+// waiting for anything. h starts out filled with 0xFFFF (the gate kernel of the
+// same forward fills it), and every element is written once by one 2-byte
+// store, so a 16-byte agent-scope load that finds no 0xFFFF element holds final
+// values: each wave loads its share of the segment's h rows right behind its
+// W2 loads, reloads any vector still unwritten, and the work-group assembles
+// the rows in LDS for the second product. The W2 stream thus follows the W1
+// stream inside one launch, and no work-group waits for a flag. Only groups
+// that lead a segment read h, and every work-group writes its chunk before it
+// reads, so the launch completes whatever the occupancy; a wait that outlasts
+// MOE_WAIT_TICKS gives up and writes NaN, so no launch can hang.
+// FUSE: top-1 combine folded in (writes y), else y_disp rows in fp32.
+template <typename DT, int MAXM, int NQ1, int NQ2, bool FUSE>
+__global__ __launch_bounds__(UP_WAVES * 64) void decode_fused_kernel(DecodeParams p, RouteParams rp, int nch,
+                                                                     int h_lds_off) {
+  using T = typename DT::T;
+  constexpr int RPW1 = DecRows<NQ1, MAXM>::RPW;
+  constexpr int RPW2 = DecRows<NQ2, MAXM>::RPW;
+  constexpr int SH1 = 6 - ilog2(RPW1 * MAXM);
+  constexpr int SH2 = 6 - ilog2(RPW2 * MAXM);
+  constexpr int WVEC = NQ2 * 64 / UP_WAVES;   // 16-byte vectors of an h row each wave loads
+  constexpr int HV = (WVEC + 63) / 64;        // ... per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = blockIdx.x / nch;
+  const int c = blockIdx.x - g * nch;
+  const long long H = p.H, F = p.F;
+  const int nch1 = p.F / (UP_WAVES * RPW1);
+  const int nch2 = p.H / (UP_WAVES * RPW2);
+  const bool do1 = c < nch1, do2 = c < nch2;
+  extern __shared__ int route_sh[];
+  const RouteLds L = route_lds(rp, route_sh);
+  __attribute__((address_space(3))) T* hs =
+      reinterpret_cast<__attribute__((address_space(3))) T*>(
+          reinterpret_cast<__attribute__((address_space(3))) char*>(
+              (__attribute__((address_space(3))) int*)route_sh) + h_lds_off);
+  __shared__ int wait_ok;
+
+  // ---- routing; this group's W1 loads go out as soon as its expert is known
+  const int f0 = c * UP_WAVES * RPW1 + wave * RPW1;
+  const int v1 = lane >> SH1;
+  const int oi1 = v1 / MAXM, om1 = v1 - (v1 / MAXM) * MAXM;
+  uint4 wv1[RPW1][NQ1];
+  T b1raw = DT::from_f(0.f);
+  const int e = route_phase1(rp, L, g, FUSE);
+  if (e >= 0 && do1) {
+    const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[e]) : reinterpret_cast<const T*>(p.w1) + (long long)e * F * H;
+    const T* b1s = p.b1p ? reinterpret_cast<const T*>(p.b1p[e]) : reinterpret_cast<const T*>(p.b1) + (long long)e * F;
+    load_rows<DT, NQ1, RPW1>(wv1, w1s + (long long)f0 * H, H);
+    b1raw = gload(b1s + f0 + oi1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (threadIdx.x == 0) wait_ok = 1;   // (published by the barriers of route_phase2)
+  int seg, r0, r1;
+  const int* lst;
+  if (!route_phase2(rp, L, p.H, g, seg, r0, r1, lst)) return;   // leads a segment: seg == e
+  const int M = min(r1 - r0, MAXM);
+  const __amdgpu_buffer_rsrc_t h_rsrc = raw_rsrc(p.h);
+
+  // ---- first product: this chunk of h = GeLU(x W1^T + b1), stored past the L2s
+  if (do1) {
+    // activation rows of the segment: loads issued before the weights are waited for
+    int rows[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) rows[m] = lds_load(lst + r0 + (m < M ? m : 0));
+    const T* x = reinterpret_cast<const T*>(p.x);
+    uint4 av[MAXM][NQ1];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+      for (int q = 0; q < NQ1; ++q)
+        av[m][q] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4_t*)(
+                                                 x + (long long)rows[m] * H + (long long)(lane + 64 * q) * DT::VEC));
+    // the weights become opaque here: otherwise the compiler starts converting
+    // them to fp32 right after their loads, which waits for them before the
+    // routing above and holds twice the registers
+#pragma unroll
+    for (int i = 0; i < RPW1; ++i)
+#pragma unroll
+      for (int q = 0; q < NQ1; ++q) {
+        u32x4_t t = __builtin_bit_cast(u32x4_t, wv1[i][q]);
+        asm volatile("" : "+v"(t));
+        wv1[i][q] = __builtin_bit_cast(uint4, t);
+      }
+    {
+      unsigned short b = __builtin_bit_cast(unsigned short, b1raw);
+      asm volatile("" : "+v"(b));
+      b1raw = __builtin_bit_cast(T, b);
+    }
+    float acc[RPW1 * MAXM];
+#pragma unroll
+    for (int i = 0; i < RPW1 * MAXM; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ1; ++q)
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) {
+        float af[DT::VEC];
+        unpack16<DT>(av[m][q], af);
+#pragma unroll
+        for (int i = 0; i < RPW1; ++i) acc[i * MAXM + m] = dot16f<DT>(wv1[i][q], af, acc[i * MAXM + m]);
+      }
+    const float s1 = wave_reduce_multi<RPW1 * MAXM>(acc);
+    if ((lane & ((1 << SH1) - 1)) == 0 && om1 < M) {
+      const T hv = DT::from_f(pin_f32(gelu_erf(s1 + DT::to_f(b1raw))));
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), h_rsrc,
+                                            (int)(((long long)(r0 + om1) * F + f0 + oi1) * 2), 0, MOE_CPOL_AGENT);
+    }
+  }
+
+  // ---- second product: W2 loads first, then this wave's share of the h rows
+  const int j0 = c * UP_WAVES * RPW2 + wave * RPW2;
+  const int v2 = lane >> SH2;
+  const int oi2 = v2 / MAXM, om2 = v2 - (v2 / MAXM) * MAXM;
+  uint4 wv2[RPW2][NQ2];
+  T b2raw = DT::from_f(0.f);
+  if (do2) {
+    const T* w2s = p.w2p ? reinterpret_cast<const T*>(p.w2p[seg]) : reinterpret_cast<const T*>(p.w2) + (long long)seg * H * F;
+    const T* b2s = p.b2p ? reinterpret_cast<const T*>(p.b2p[seg]) : reinterpret_cast<const T*>(p.b2) + (long long)seg * H;
+    load_rows<DT, NQ2, RPW2>(wv2, w2s + (long long)j0 * F, F);
+    b2raw = gload(b2s + j0 + oi2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // vector u of row m: elements (wave * WVEC + u * 64 + lane) * VEC .. + VEC - 1
+  uint4 hv[MAXM][HV];
+  auto h_off = [&](int m, int u) {
+    return (int)(((long long)(r0 + m) * F + (long long)(wave * WVEC + u * 64 + lane) * DT::VEC) * 2);
+  };
+  auto h_mine = [&](int m, int u) { return m < M && u * 64 + lane < WVEC; };
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+    for (int u = 0; u < HV; ++u)
+      if (h_mine(m, u))
+        hv[m][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(h_rsrc, h_off(m, u), 0,
+                                                                                   MOE_CPOL_AGENT));
+  {
+    // normally every element is written by now (its producer's W1 data came
+    // in before this wave's W2 data); reload whatever is not
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+      bool miss = false;
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+        for (int u = 0; u < HV; ++u) miss |= h_mine(m, u) && has_unwritten(hv[m][u]);
+      if (__ballot(miss) == 0) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > MOE_WAIT_TICKS) {
+        if (lane == 0) wait_ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+        for (int u = 0; u < HV; ++u)
+          if (h_mine(m, u) && has_unwritten(hv[m][u]))
+            hv[m][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(h_rsrc, h_off(m, u), 0,
+                                                                                       MOE_CPOL_AGENT));
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+    for (int u = 0; u < HV; ++u)
+      if (h_mine(m, u))
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(
+            hs + (long long)m * F + (long long)(wave * WVEC + u * 64 + lane) * DT::VEC) =
+            __builtin_bit_cast(u32x4_t, hv[m][u]);
+  __syncthreads();
+  if (!do2) return;
+#pragma unroll
+  for (int i = 0; i < RPW2; ++i)
+#pragma unroll
+    for (int q = 0; q < NQ2; ++q) {   // (as for W1: no conversion before the loads are needed)
+      u32x4_t t = __builtin_bit_cast(u32x4_t, wv2[i][q]);
+      asm volatile("" : "+v"(t));
+      wv2[i][q] = __builtin_bit_cast(uint4, t);
+    }
+  {
+    unsigned short b = __builtin_bit_cast(unsigned short, b2raw);
+    asm volatile("" : "+v"(b));
+    b2raw = __builtin_bit_cast(T, b);
+  }
+  const float s2 = dot_rows_lds<DT, MAXM, NQ2, RPW2>(wv2, hs, (int)F);
+  if ((lane & ((1 << SH2) - 1)) == 0 && om2 < M) {
+    const float yv = wait_ok ? s2 + DT::to_f(b2raw) : __builtin_nanf("");
+    if constexpr (FUSE) {
+      const int t_out = lds_load(lst + r0 + om2);
+      const float wt = __builtin_bit_cast(float, lds_load(reinterpret_cast<const int*>(L.lw) + t_out));
+      reinterpret_cast<T*>(p.out)[(long long)t_out * H + j0 + oi2] = DT::from_f(pin_f32(fmaf(wt, yv, 0.f)));
+    } else {
+      reinterpret_cast<float*>(p.out)[(long long)(r0 + om2) * H + j0 + oi2] = yv;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 static int nq_of(int K, int vec) { return K / (64 * vec); }
 
@@ -459,6 +711,66 @@ static hipError_t launch_dt(bool up, int maxm, const DecodeParams& p, const Rout
     case 4: return launch_m<DT, 4>(up, p, rp, grid_segs, fuse, s, ev);
     case 8: return launch_m<DT, 8>(up, p, rp, grid_segs, fuse, s, ev);
   }
+  return hipErrorInvalidValue;
+}
+
+template <typename DT, int MAXM, int NQ1, int NQ2>
+static hipError_t launch_fused_t(const DecodeParams& p, const RouteParams& rp, int grid_segs, bool fuse,
+                                 hipStream_t s, LaunchEv ev) {
+  constexpr int RPW1 = DecRows<NQ1, MAXM>::RPW, RPW2 = DecRows<NQ2, MAXM>::RPW;
+  const int nch = std::max(p.F / (UP_WAVES * RPW1), p.H / (UP_WAVES * RPW2));
+  const int grid = grid_segs * nch;
+  const int h_off = (int)((sizeof(int) * route_lds_ints(rp.T, rp.k, rp.R_max) + 15) / 16 * 16);
+  const size_t lds = (size_t)h_off + (size_t)MAXM * p.F * sizeof(typename DT::T);
+  if (fuse)
+    MOE_LAUNCH((decode_fused_kernel<DT, MAXM, NQ1, NQ2, true>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start,
+               ev.stop, p, rp, nch, h_off);
+  else
+    MOE_LAUNCH((decode_fused_kernel<DT, MAXM, NQ1, NQ2, false>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start,
+               ev.stop, p, rp, nch, h_off);
+  return hipGetLastError();
+}
+
+template <typename DT, int MAXM>
+static hipError_t launch_fused_m(const DecodeParams& p, const RouteParams& rp, int grid_segs, bool fuse,
+                                 hipStream_t s, LaunchEv ev) {
+  const int nq1 = nq_of(p.H, DT::VEC), nq2 = nq_of(p.F, DT::VEC);
+#define FCASE(Q1, Q2) \
+  if (nq1 == Q1 && nq2 == Q2) return launch_fused_t<DT, MAXM, Q1, Q2>(p, rp, grid_segs, fuse, s, ev);
+  FCASE(1, 4) FCASE(2, 8) FCASE(4, 16) FCASE(1, 2) FCASE(2, 4) FCASE(4, 8) FCASE(1, 1) FCASE(2, 2) FCASE(4, 4)
+#undef FCASE
+  return hipErrorInvalidValue;
+}
+
+// Shapes the one-launch decode kernel is built for: H and F from the streaming
+// kernels' set with F / H in {1, 2, 4} (F = 4H is the pages' model shape), and
+// the staged h rows (MAXM x F in the I/O dtype) within 32 KB of LDS.
+bool decode_fused_supported(int dtype, int H, int F, int maxm) {
+  if (dtype == DT_F32 || !decode_supported(dtype, H, F)) return false;
+  if (!(F == H || F == 2 * H || F == 4 * H) || H > 2048) return false;
+  if (maxm != 1 && maxm != 2 && maxm != 4 && maxm != 8) return false;
+  return (long long)maxm * F * 2 <= 32768;
+}
+
+hipError_t launch_decode_fused(int dtype, int maxm, const DecodeParams& p, const RouteParams& rp, int grid_segs,
+                               bool fuse_combine, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (grid_segs <= 0) return hipSuccess;
+  if (!rp.z || (fuse_combine && !p.out)) return hipErrorInvalidValue;
+  if (!decode_fused_supported(dtype, p.H, p.F, maxm)) return hipErrorInvalidValue;
+  const LaunchEv ev{ev0, ev1};
+#define FM(DT_)                                                                            \
+  switch (maxm) {                                                                          \
+    case 1: return launch_fused_m<DT_, 1>(p, rp, grid_segs, fuse_combine, s, ev);   \
+    case 2: return launch_fused_m<DT_, 2>(p, rp, grid_segs, fuse_combine, s, ev);   \
+    case 4: return launch_fused_m<DT_, 4>(p, rp, grid_segs, fuse_combine, s, ev);   \
+    case 8: return launch_fused_m<DT_, 8>(p, rp, grid_segs, fuse_combine, s, ev);   \
+  }
+  if (dtype == DT_F16) {
+    FM(DtF16)
+  } else {
+    FM(DtBF16)
+  }
+#undef FM
   return hipErrorInvalidValue;
 }
 

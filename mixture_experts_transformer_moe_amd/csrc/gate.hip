@@ -16,8 +16,13 @@ namespace moe {
 template <typename DT, int NQ, int EB>
 __global__ __launch_bounds__(64) void gate_logits_fma_kernel(
     const typename DT::T* __restrict__ x, const typename DT::T* __restrict__ wg,
-    const float* __restrict__ bias, float* __restrict__ z, int T, int H, int E) {
+    const float* __restrict__ bias, float* __restrict__ z, int T, int H, int E, unsigned* __restrict__ fill,
+    int nfill) {
   constexpr int NV = EB * GATE_TB;                 // logits per wave
+  if (fill) {   // spread over the blocks
+    const int b = blockIdx.y * gridDim.x + blockIdx.x, nb = gridDim.x * gridDim.y;
+    for (int i = b * 64 + lane_id(); i < nfill; i += nb * 64) fill[i] = 0xFFFFFFFFu;
+  }
   constexpr int SH = 6 - (NV == 8 ? 3 : NV == 16 ? 4 : 5);
   const int lane = lane_id();
   const int t0 = blockIdx.x * GATE_TB;
@@ -71,15 +76,15 @@ __global__ __launch_bounds__(256) void softmax_topk_kernel(const float* z, int T
 
 template <typename DT, int EB>
 static hipError_t launch_gate_fma_eb(const void* x, const void* wg, const float* bias, float* z, int T, int H, int E,
-                                     int nq, hipStream_t s) {
+                                     int nq, hipStream_t s, unsigned* fill, int nfill) {
   using T_ = typename DT::T;
   dim3 grid((T + GATE_TB - 1) / GATE_TB, (E + EB - 1) / EB);
   if (nq == 1)
     hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 1, EB>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg, bias,
-                       z, T, H, E);
+                       z, T, H, E, fill, nfill);
   else
     hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 2, EB>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg, bias,
-                       z, T, H, E);
+                       z, T, H, E, fill, nfill);
   return hipGetLastError();
 }
 
@@ -95,27 +100,27 @@ static int gate_experts_per_wave(int T, int E, int H, int dtype) {
 
 template <typename DT>
 static hipError_t launch_gate_fma_t(const void* x, const void* wg, const float* bias, float* z, int T, int H, int E,
-                                    hipStream_t s) {
+                                    hipStream_t s, unsigned* fill, int nfill) {
   using T_ = typename DT::T;
   const int nq = (H % (64 * DT::VEC) == 0) ? H / (64 * DT::VEC) : 0;
   const int eb = gate_experts_per_wave(T, E, H, sizeof(T_) == 4 ? DT_F32 : DT_F16);
   if (nq == 1 || nq == 2) {
-    if (eb == 1) return launch_gate_fma_eb<DT, 1>(x, wg, bias, z, T, H, E, nq, s);
-    if (eb == 2) return launch_gate_fma_eb<DT, 2>(x, wg, bias, z, T, H, E, nq, s);
-    return launch_gate_fma_eb<DT, GATE_EB>(x, wg, bias, z, T, H, E, nq, s);
+    if (eb == 1) return launch_gate_fma_eb<DT, 1>(x, wg, bias, z, T, H, E, nq, s, fill, nfill);
+    if (eb == 2) return launch_gate_fma_eb<DT, 2>(x, wg, bias, z, T, H, E, nq, s, fill, nfill);
+    return launch_gate_fma_eb<DT, GATE_EB>(x, wg, bias, z, T, H, E, nq, s, fill, nfill);
   }
   dim3 grid((T + GATE_TB - 1) / GATE_TB, (E + GATE_EB - 1) / GATE_EB);
   hipLaunchKernelGGL((gate_logits_fma_kernel<DT, 0, GATE_EB>), grid, dim3(64), 0, s, (const T_*)x, (const T_*)wg,
-                     bias, z, T, H, E);
+                     bias, z, T, H, E, fill, nfill);
   return hipGetLastError();
 }
 
 hipError_t launch_gate_logits_fma(int dtype, const void* x, const void* wg, const float* bias, float* z,
-                                  int T, int H, int E, hipStream_t s) {
+                                  int T, int H, int E, hipStream_t s, unsigned* fill, int nfill) {
   switch (dtype) {
-    case DT_F32: return launch_gate_fma_t<DtF32>(x, wg, bias, z, T, H, E, s);
-    case DT_F16: return launch_gate_fma_t<DtF16>(x, wg, bias, z, T, H, E, s);
-    default: return launch_gate_fma_t<DtBF16>(x, wg, bias, z, T, H, E, s);
+    case DT_F32: return launch_gate_fma_t<DtF32>(x, wg, bias, z, T, H, E, s, fill, nfill);
+    case DT_F16: return launch_gate_fma_t<DtF16>(x, wg, bias, z, T, H, E, s, fill, nfill);
+    default: return launch_gate_fma_t<DtBF16>(x, wg, bias, z, T, H, E, s, fill, nfill);
   }
 }
 

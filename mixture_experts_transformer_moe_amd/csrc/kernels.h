@@ -10,8 +10,10 @@
 namespace moe {
 
 // gate.hip
+// fill (nullable): nfill 32-bit words set to 0xFFFFFFFF by the launch (the
+// one-launch decode kernel's hidden rows, marked unwritten in the launch before it)
 hipError_t launch_gate_logits_fma(int dtype, const void* x, const void* wg, const float* bias, float* z,
-                                  int T, int H, int E, hipStream_t s);
+                                  int T, int H, int E, hipStream_t s, unsigned* fill = nullptr, int nfill = 0);
 // zsplit > 1: z holds that many partial logit sums, T * E floats apart (see GemmParams::ksplit)
 hipError_t launch_softmax_topk(const float* z, int T, int E, int k, int renorm, int* idx, float* w,
                                float* probs, hipStream_t s, int zsplit = 1);
@@ -50,6 +52,11 @@ hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, const RouteParams* rp = nullptr);
 hipError_t launch_decode_down(int dtype, int maxm, const DecodeParams& p, int grid_segs, bool fuse_combine,
                               hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// Both expert products in one launch (routing inside, as launch_decode_up with rp);
+// p.h must hold 0xFFFF in every 16-bit element at launch (the gate kernel fills it).
+bool decode_fused_supported(int dtype, int H, int F, int maxm);
+hipError_t launch_decode_fused(int dtype, int maxm, const DecodeParams& p, const RouteParams& rp, int grid_segs,
+                               bool fuse_combine, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // combine.hip: y[t] = sum_j w[t,j] ysrc[token_slot[t,j]] (+ dense[t]); ysrc [*, H], dense [T, H] fp32
 hipError_t launch_combine(int dtype, const float* ysrc, const int* token_slot, const float* w, int k,

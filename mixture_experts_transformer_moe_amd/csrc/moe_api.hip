@@ -111,6 +111,7 @@ struct Plan {
   bool exp_decode;   // streaming kernels for segments of <= 8 rows, else grouped MFMA GEMM
   bool fold_combine; // top-1 standard layer on the decode path: the expert kernel writes y
   bool route_in_up;  // decode path with a tiny batch: the first expert kernel does the dispatch
+  bool fused_decode; // ... and both expert products run in one launch (h marked unwritten by the gate)
   int exp_maxm;
   int BM, BN1, BN2, mt_bound;
   // dense MLP
@@ -144,7 +145,8 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "residual mode routes one expert per token (top_k must be 1)");
   if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_F16 && d->dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown dtype");
-  if (d->flags & ~MOE_FLAG_RENORM_TOPK) return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flag bits");
+  if (d->flags & ~(MOE_FLAG_RENORM_TOPK | MOE_FLAG_DECODE_ONE_LAUNCH))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flag bits");
   if (d->hidden % 64 || d->ffn % 64) return fail(MOE_ERR_UNSUPPORTED, "hidden and ffn must be multiples of 64");
   if (d->num_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "num_experts > %d", kMaxExperts);
   if (d->num_tokens * (int64_t)d->top_k > kMaxAssignments)
@@ -181,6 +183,9 @@ moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
   p.exp_decode = seg_rows <= 8 && decode_supported(p.dtype, p.H, p.F);
   p.fold_combine = p.exp_decode && p.k == 1 && !p.residual;
   p.route_in_up = p.exp_decode && route_in_decode_supported((int)p.T, p.k, p.E, p.E_loc);
+  // one launch for both expert products: the vector-ALU gate kernel marks its h rows unwritten
+  p.fused_decode = (d->flags & MOE_FLAG_DECODE_ONE_LAUNCH) && p.route_in_up && !p.gate_mfma &&
+                   decode_fused_supported(p.dtype, p.H, p.F, p.exp_maxm);
   // matrix-core gate: each K step of a work-group waits on its loads, so a
   // short tile over all of K is latency-bound. Column tiles of 128 experts (x
   // read once per token tile); the tallest row tile and the fewest slices of K
@@ -346,7 +351,7 @@ moe_status_t check_weights(const Plan& p, const moe_layer_weights_t* w, bool exp
 
 // ---------------------------------------------------------------- launch steps
 moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, const float* gate_b, float* z,
-                             hipStream_t s) {
+                             hipStream_t s, unsigned* fill = nullptr, int nfill = 0) {
   if (p.gate_mfma) {
     GemmParams g{};
     g.A = x;
@@ -363,7 +368,8 @@ moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, c
     const int grid = (int)((p.T + p.gate_BM - 1) / p.gate_BM) * g.n_ntiles;
     HIP_TRY(launch_grouped_gemm(p.dtype, EPI_F32, true, p.gate_BM, p.gate_BN, g, grid, s), "gate logits (mfma)");
   } else {
-    HIP_TRY(launch_gate_logits_fma(p.dtype, x, gate_w, gate_b, z, (int)p.T, p.H, p.E, s), "gate logits");
+    HIP_TRY(launch_gate_logits_fma(p.dtype, x, gate_w, gate_b, z, (int)p.T, p.H, p.E, s, fill, nfill),
+            "gate logits");
   }
   return MOE_OK;
 }
@@ -440,6 +446,13 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
     const int gsegs = (int)std::min<int64_t>(p.E_loc, p.R_max);
     // routed in the kernel: one group of work-groups per assignment (see route_phase1)
     const int gsegs_up = route ? (int)(p.T * p.k) : gsegs;
+    if (route && p.fused_decode) {
+      HIP_TRY(launch_decode_fused(p.dtype, p.exp_maxm, d, *route, gsegs_up, y_fold != nullptr, s, e.up_start,
+                                  e.up_stop),
+              "expert ffn (decode, one launch)");
+      ST_TRY(record(split, s));
+      return MOE_OK;
+    }
     HIP_TRY(launch_decode_up(p.dtype, p.exp_maxm, d, gsegs_up, s, e.up_start, e.up_stop, route),
             "expert ffn up (decode)");
     ST_TRY(record(split, s));
@@ -624,7 +637,8 @@ moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out) {
   // gate; dispatch (one block, or softmax/top-k + count, scan, scatter); two
   // expert kernels (the GEMMs' tile lists come from the dispatch); the dense
   // MLP's two unless inside the expert GEMMs; combine
-  out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) + 2 +
+  out->experts_one_launch = p.fused_decode ? 1 : 0;
+  out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) + (p.fused_decode ? 1 : 2) +
                   ((p.residual && !p.dense_in_experts) ? 2 : 0) + (p.fold_combine ? 0 : 1);
   return MOE_OK;
 }
@@ -744,7 +758,9 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
 
   void* y_fold = p.fold_combine ? y : nullptr;
   ST_TRY(record(e.gate_begin, stream));
-  ST_TRY(run_gate_logits(p, x, w->gate_w, w->gate_b, z, stream));
+  // the one-launch decode kernel finds its hidden rows marked unwritten (0xFFFF)
+  ST_TRY(run_gate_logits(p, x, w->gate_w, w->gate_b, z, stream, p.fused_decode ? wsp<unsigned>(ws, p.o_h) : nullptr,
+                         p.fused_decode ? (int)(p.R_max * p.F * (int64_t)p.esz / 4) : 0));
   ST_TRY(record(e.gate_end, stream));
   ST_TRY(record(e.dispatch_begin, stream));
   RouteParams rp{};

@@ -54,6 +54,7 @@ class LayerShape:
     zipf_s: Optional[float] = None
     e_lo: int = 0          # first local expert
     renorm: bool = False   # renormalise the top-k weights
+    one_launch: bool = False  # decode path: both expert products in one launch
 
     @property
     def torch_dtype(self) -> torch.dtype:

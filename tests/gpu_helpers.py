@@ -27,6 +27,11 @@ def host(t):
     return W.to_host_f64_ready(t)
 
 
+def host_t(t):
+    """Host copy as a torch tensor (bf16 widened to f32, like host())."""
+    return torch.as_tensor(host(t))
+
+
 def device_case(shape, seed=0, x_seed=None):
     x = W.make_x(shape, seed if x_seed is None else x_seed, device="cuda")
     w = W.make_weights(shape, seed, device="cuda")

@@ -125,6 +125,12 @@ def test_layer_plan_paths():
                pl["launches"])
         assert got == (gate, experts, disp, comb, launches), (name, pl)
         assert pl["dense_in_expert_kernels"] == (name == "prmoe_residual"), (name, pl)
+        assert not pl["experts_one_launch"], (name, pl)
+    # the one-launch decode kernel only on request, and only on the routed decode path
+    one = B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["decode_350m_moe128"].with_(one_launch=True)))
+    assert one["experts_one_launch"] and one["launches"] == 2
+    assert not B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["prefill_1p3b_moe128"].with_(one_launch=True)))[
+        "experts_one_launch"]
     # tiles: 64-row tiles for segments of <= 64 rows; 160 x 256 for the 24B share's 320-row segments
     assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["prefill_1p3b_moe128"]))["tile"] == (64, 128, 128)
     assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["share_24b_moe128"]))["tile"] == (160, 256, 256)
