@@ -521,7 +521,7 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -
                 ffn_phase={"us": round((kern_ms["up"] + kern_ms["down"]) * 1e3 / args.steps, 2),
                            "GB/s": round((win_bytes["up"] + win_bytes["down"]) /
                                          ((kern_ms["up"] + kern_ms["down"]) / 1e3) / 1e9, 1)})
-    roof["traffic"] = measured_traffic(shape.name, kern)
+    roof["traffic"] = measured_traffic(shape.name + ("_one_launch" if shape.one_launch else ""), kern)
 
     res = {
         "tokens_per_s": round(tokens_per_s, 1),
