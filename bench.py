@@ -102,6 +102,7 @@ class ClockSampler:
     def __init__(self, period_s: float = 0.01):
         import threading
         self.mhz, self.err, self.period = [], None, period_s
+        self.source = "amdsmi"
         self._stop = threading.Event()
         self.active = threading.Event()
         self._handle = None
@@ -119,7 +120,21 @@ class ClockSampler:
         self._thread = threading.Thread(target=self._run, daemon=True)
 
     def _read(self) -> float:
+        """The graphics clock in MHz from the firmware's metrics table (the
+        highest per-XCD value when it lists them), else the clock info."""
+        try:
+            m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+            for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+                v = m.get(key)
+                if isinstance(v, (list, tuple)):
+                    v = max([float(c) for c in v if isinstance(c, (int, float)) and 0 < c < 65535] or [0])
+                if isinstance(v, (int, float)) and 0 < v < 65535:
+                    self.source = f"amdsmi gpu metrics {key}"
+                    return float(v)
+        except Exception:
+            pass
         info = self._smi.amdsmi_get_clock_info(self._handle, self._smi.AmdSmiClkType.GFX)
+        self.source = "amdsmi clock info gfx clk"
         return float(info["clk"])
 
     def _run(self):
@@ -152,9 +167,14 @@ class ClockSampler:
         if not self.mhz:
             return {"mhz_median": None, "samples": 0, "source": "amdsmi gfx clock", "error": self.err}
         v = np.array(self.mhz)
+        if np.median(v) < 500:   # below the part's lowest clock level: not a live reading of this device
+            return {"mhz_median": None, "samples": int(v.size), "source": self.source,
+                    "error": f"reads {float(np.median(v)):.0f} MHz while the passes run, below the part's "
+                             "500 MHz minimum: not a live clock (the clock under load is in the counter "
+                             "summaries, from GRBM_GUI_ACTIVE)"}
         return {"mhz_median": float(np.median(v)), "mhz_min": float(v.min()), "mhz_max": float(v.max()),
-                "samples": int(v.size), "source": "amdsmi gfx clock, sampled every 10 ms during the timed and "
-                                                  "per-step passes"}
+                "samples": int(v.size), "source": self.source + ", sampled during the timed, graph and per-step "
+                                                                "passes"}
 
 
 def main():
@@ -177,6 +197,8 @@ def main():
                     help="time only --workload (no extra grouped-GEMM workloads in the same run)")
     ap.add_argument("--one-launch", action="store_true",
                     help="decode path: both expert products in one launch (MOE_FLAG_DECODE_ONE_LAUNCH)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager launches only (no graph replay of the K steps)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the pass that times the expert kernels with launch-recorded events")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -229,6 +251,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
+        "timing": head["timing"],
+        "eager_ms_per_step": head["eager_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -262,7 +286,8 @@ def config_entry(r: dict, clock: dict) -> dict:
     lay = r["layer"]
     bound = lay["graded_bound"]
     frac = lay["mfma_frac"] if bound == "mfma" else lay["hbm_frac"]
-    e = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"], "step_us": r["step_us"],
+    e = {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"], "timing": r["timing"],
+         "eager_ms_per_step": r["eager_ms_per_step"], "step_us": r["step_us"],
          "f_hbm": lay["hbm_frac"], "f_mfma": lay["mfma_frac"],
          "graded": {"bound": bound, "frac": float(frac),
                     "target": 0.5 if bound == "mfma" else 0.7},
@@ -373,6 +398,35 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -
     ms_per_step = ms_total / args.steps
     tokens_per_s = shape.T * args.steps / (ms_total / 1e3)
     print(f"[bench] {shape.name}: timed pass done: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+
+    # ---- the same K steps captured once in a HIP graph and replayed: the GPU's
+    # time for them without the host's launch cost (a decode step is ~30 us of
+    # GPU work, the same order as the Python + runtime cost of enqueuing it)
+    graph_ms = None
+    if not args.no_graph and not stores:
+        side = torch.cuda.Stream()      # default priority, like every stream here
+        side.wait_stream(stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(args.steps):
+                li, bi = lb(i)
+                layers[li].forward(xs[bi], y)     # the capture stream is current here
+        graph.replay()                            # warm replay
+        torch.cuda.synchronize()
+        if clock:
+            clock.active.set()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        if clock:
+            clock.active.clear()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del graph
+        print(f"[bench] {shape.name}: graph replay {graph_ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
     hip = _Hip()
     # ---- per-step distribution: an event pair around each step (same steps, same stream)
@@ -523,9 +577,18 @@ def run_layer(shape, args, *, cpu_budget: float, store_slots=None, clock=None) -
                                          ((kern_ms["up"] + kern_ms["down"]) / 1e3) / 1e9, 1)})
     roof["traffic"] = measured_traffic(shape.name + ("_one_launch" if shape.one_launch else ""), kern)
 
+    # value: the graph replay of the K steps when taken (the eager rate is
+    # reported beside it and depends on the host's launch speed)
+    eager_ms = ms_per_step
+    if graph_ms is not None:
+        ms_per_step = graph_ms
+        tokens_per_s = shape.T / (graph_ms / 1e3)
     res = {
         "tokens_per_s": round(tokens_per_s, 1),
         "ms_per_step": round(ms_per_step, 5),
+        "timing": ("K steps replayed from one captured HIP graph" if graph_ms is not None
+                   else "K steps launched eagerly"),
+        "eager_ms_per_step": round(eager_ms, 5),
         "step_us": step_us,
         "plan": plan,
         "config": {"workload": shape.name + ("_one_launch" if shape.one_launch else ""), "tokens": shape.T,

@@ -24,6 +24,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # no packed fp32 instructions from the compiler (v_pk_* fp32 forms)
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # the first 16 dwords of every kernel's arguments arrive in SGPRs (no
+          # dependent scalar load at the start of each launch)
+          "-mllvm", "-amdgpu-kernarg-preload-count=16",
           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", HERE]
 
 

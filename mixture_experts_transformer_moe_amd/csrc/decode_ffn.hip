@@ -296,7 +296,7 @@ __device__ inline int lds_load(const int* p) { return *(const __attribute__((add
 // the row's token and gate weight) is issued before or with the weight loads,
 // so only the weight stream itself is left to wait for.
 template <typename DT, int MAXM, int NQ>
-__global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(DecodeParams p, RouteParams rp) {
+__global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(RouteParams rp, DecodeParams p) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
   constexpr int N = RPW * MAXM;
@@ -674,7 +674,7 @@ static hipError_t launch_up_t(const DecodeParams& p, const RouteParams& rp, int 
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
   const int grid = grid_segs * (p.F / (UP_WAVES * RPW));
   const size_t lds = rp.z ? sizeof(int) * route_lds_ints(rp.T, rp.k, rp.R_max) : 0;
-  MOE_LAUNCH((decode_up_kernel<DT, MAXM, NQ>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start, ev.stop, p, rp);
+  MOE_LAUNCH((decode_up_kernel<DT, MAXM, NQ>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start, ev.stop, rp, p);
   return hipGetLastError();
 }
 

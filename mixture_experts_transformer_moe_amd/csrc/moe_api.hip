@@ -126,7 +126,29 @@ struct Plan {
   size_t total;
 };
 
+moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl);
+
+// The plan of the last descriptor this thread validated: a decode loop calls the
+// layer with the same descriptor every step, and the plan is a pure function of
+// it (byte-equal descriptors have equal fields).
 moe_status_t validate(const moe_layer_desc_t* d, Plan* pl) {
+  thread_local moe_layer_desc_t last_d;
+  thread_local Plan last_p;
+  thread_local bool have = false;
+  if (d && have && memcmp(d, &last_d, sizeof(*d)) == 0) {
+    *pl = last_p;
+    return MOE_OK;
+  }
+  const moe_status_t st = validate_uncached(d, pl);
+  if (st == MOE_OK) {
+    memcpy(&last_d, d, sizeof(*d));
+    last_p = *pl;
+    have = true;
+  }
+  return st;
+}
+
+moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl) {
   if (!d) return fail(MOE_ERR_INVALID_ARGUMENT, "descriptor is NULL");
   if (d->num_tokens < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_tokens < 0");
   if (d->hidden <= 0 || d->ffn <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "hidden and ffn must be > 0");
