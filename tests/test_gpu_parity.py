@@ -59,6 +59,12 @@ CASES = {
     # 150 rows): every activation load of the first GEMM, spare chunks included,
     # must stay inside x's 150 rows
     "gemm_bm160_t150": W.LayerShape("g160t", T=150, H=256, F=512, E=2, E_loc=2, k=2, cf=2.0, dtype="f16"),
+    # ping-pong tiles at widths that are multiples of 256 but not of 512: 160 x
+    # 256 tiles of a 768-wide first product, and a residual layer with both
+    # products and the dense MLP on 128 x 256 tiles (H = F = 768, bf16)
+    "gemm_bm160_bn256": W.LayerShape("g160n", T=1024, H=512, F=768, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
+    "residual_bm128_bn256": W.LayerShape("r128n", T=1024, H=768, F=768, E=8, E_loc=8, k=1, cf=1.0, dtype="bf16",
+                                         mlp_type="residual"),
     # edge cases: the maximum expert count (8 logits per lane in the top-k), a
     # ragged token count (gate token blocks of 8), heavy drops (cf = 0.1), one
     # token through a residual layer, and a share of a single local expert
