@@ -157,6 +157,72 @@ __device__ inline void gemm_epilogue(const GemmParams& p, const float4_t (&acc)[
   }
 }
 
+// Epilogue through LDS for 64-column wave blocks (the ping-pong tiles): the same
+// values as gemm_epilogue, but the wave first writes 128 bytes of each of its
+// 16 TM rows to its own LDS area (the 16-byte columns XOR-swizzled by row) and
+// then stores whole 128-byte row pieces, eight rows per store instruction,
+// where the register layout of the accumulators gives 32-byte (2-byte outputs)
+// or 64-byte (fp32) pieces of sixteen rows per instruction. 2-byte GeLU outputs
+// take one pass (64 columns), fp32 outputs two (32 columns each). The caller
+// guarantees that no wave still reads the LDS the area overlaps.
+template <typename DT, int EPI, typename BiasT, int TM>
+__device__ inline void gemm_epilogue_lds(const GemmParams& p, const float4_t (&acc)[4][TM], int seg, int n0, int m0,
+                                         int r1, int lane, char* area) {
+  using T = typename DT::T;
+  constexpr bool GELU = EPI == EPI_GELU;
+  static_assert(!GELU || sizeof(T) == 2, "GeLU outputs of 2 bytes");
+  constexpr int ESZ = GELU ? 2 : 4;
+  constexpr int CPP = 128 / ESZ;              // columns per pass: one 128-byte row piece
+  constexpr int NP = 64 / CPP;
+  const bool extra = seg == p.nseg;
+  char* Cout = reinterpret_cast<char*>(extra ? p.C2 : p.C);
+  const BiasT* bias = extra     ? reinterpret_cast<const BiasT*>(p.bias2)
+                      : p.biasp ? reinterpret_cast<const BiasT*>(p.biasp[seg])
+                      : p.bias  ? reinterpret_cast<const BiasT*>(p.bias) + (long long)seg * p.bias_stride
+                                : nullptr;
+  const int quad = lane >> 4;
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+#pragma unroll
+    for (int ii = 0; ii < 4 / NP; ++ii) {
+      const int i = ps * (4 / NP) + ii;
+      const int n = i * 16 + quad * 4;        // column within the wave's block
+      const int byte = (n - ps * CPP) * ESZ;  // within this pass's row piece
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bv[q] = load_bias<BiasT>(bias, n0 + n + q);
+      }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int m = j * 16 + (lane & 15);
+        char* dst = area + m * 128 + ((((byte >> 4) ^ (m & 7))) << 4) + (byte & 15);
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] + bv[q];
+        if constexpr (GELU) {
+          T o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = DT::from_f(pin_f32(gelu_erf(v[q])));
+          *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o);
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    // LDS executes a wave's accesses in order: the reads below see every lane's
+    // writes above, and the next pass's writes follow these reads
+#pragma unroll
+    for (int r = 0; r < TM * 2; ++r) {
+      const int m = r * 8 + (lane >> 3);
+      const int c = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(area + m * 128 + ((c ^ (m & 7)) << 4));
+      if (m0 + m < r1)
+        *reinterpret_cast<uint4*>(Cout + ((long long)(m0 + m) * p.N + n0 + ps * CPP) * ESZ + c * 16) = v;
+    }
+  }
+}
+
 // Which output tile a work-group computes: (segment, column tile, row tile) and
 // the segment's row range. Returns false past the end of the tile list.
 __device__ inline bool gemm_tile(const GemmParams& p, int BM, int& seg, int& nt, int& mt, int& r0, int& r1) {
@@ -580,7 +646,16 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
 #undef DM_FRAGS
 #undef DM_MATH
 #undef DM_BAR
-  gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + g * TM * 16, r1, lane);
+  if constexpr (EPI != EPI_GELU || sizeof(T) == 2) {
+    // every wave is past its last fragment read of the K loop's buffers before
+    // any wave overwrites them with its output rows (8 x 16 TM rows of 128 B)
+    static_assert(8 * TM * 16 * 128 <= 3 * STAGE, "output blocks fit the K-step buffers");
+    __syncthreads();
+    gemm_epilogue_lds<DT, EPI, BiasT, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + g * TM * 16, r1, lane,
+                                          smem + wave * (TM * 16 * 128));
+  } else {
+    gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + g * TM * 16, r1, lane);
+  }
 }
 
 // ---------------------------------------------------------------- plan kernel
