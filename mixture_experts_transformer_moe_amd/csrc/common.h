@@ -194,6 +194,18 @@ struct GemmParams {
   // writes its partial sums to C + s * c_split (bias in slice 0 only); 0 or 1: none
   int ksplit;
   long long c_split;
+  // optional top-1 combine folded into an fp32 epilogue: row r of the row space
+  // is token fold_token[r], and the epilogue writes fold_y[token] =
+  // round(fold_w[token] * value) in the I/O dtype (zero_esz bytes) instead of C.
+  // null: none
+  void* fold_y;
+  const int* fold_token;
+  const float* fold_w;
+  // optional: after their K loops the launch's work-groups also zero the zero_T
+  // rows of zero_y (zero_N elements of zero_esz bytes each), row t by work-group
+  // t mod (gridDim.x * gridDim.y). null: none
+  void* zero_y;
+  int zero_T, zero_esz, zero_N;
   // host only: every expert weight tile is read by at most two work-groups
   // (segments of at most two row tiles), so the launch picks the variant that
   // streams the expert weights with non-temporal loads

@@ -113,9 +113,11 @@ __device__ inline float load_bias<__bf16>(const __bf16* b, int n) {
 // Epilogue of a wave's TN x TM accumulator tiles: lane holds
 // D[n = n0 + 16 i + 4 (lane / 16) + q][m = m0 + 16 j + lane % 16], q = 0..3;
 // rows at or past r1 are not stored.
+// With the combine folded in (p.fold_y): ftok[j] / fw[j] are the token and gate
+// weight of this lane's row m0 + 16 j + lane % 16 (fold_prefetch).
 template <typename DT, int EPI, typename BiasT, int TN, int TM>
 __device__ inline void gemm_epilogue(const GemmParams& p, const float4_t (&acc)[TN][TM], int seg, int n0, int m0,
-                                     int r1, int lane) {
+                                     int r1, int lane, const int (&ftok)[TM], const float (&fw)[TM]) {
   using T = typename DT::T;
   const bool extra = seg == p.nseg;
   void* Cout = extra ? p.C2 : p.C;
@@ -149,11 +151,55 @@ __device__ inline void gemm_epilogue(const GemmParams& p, const float4_t (&acc)[
 #pragma unroll
           for (int q = 0; q < 4; ++q) dst[q] = o[q];
         }
+      } else if (p.fold_y && !extra) {
+        // top-1 combine: this row is one token's only kept choice; the same
+        // fp32 product with the gate weight, rounded once, as the combine kernel
+        const int t = ftok[j];
+        const float wt = fw[j];
+        T o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = DT::from_f(pin_f32(fmaf(wt, v[q], 0.f)));
+        T* dst = reinterpret_cast<T*>(p.fold_y) + (long long)t * p.N + n;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o);
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        }
       } else {
         float* dst = reinterpret_cast<float*>(Cout) + (long long)r * p.N + n;
         *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
+  }
+}
+
+// Token and gate weight of each of this lane's rows m0 + 16 j + lane % 16 for
+// the folded combine, loaded before the K loop so that the epilogue does not
+// wait for them (rows past r1 read nothing).
+template <int TM>
+__device__ inline void fold_prefetch(const GemmParams& p, bool fold, int m0, int r1, int lane, int (&ftok)[TM],
+                                     float (&fw)[TM]) {
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int r = m0 + j * 16 + (lane & 15);
+    ftok[j] = (fold && r < r1) ? p.fold_token[r] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int r = m0 + j * 16 + (lane & 15);
+    fw[j] = (fold && r < r1) ? p.fold_w[ftok[j]] : 0.f;
+  }
+}
+
+// Zeroing of p.zero_y (the layer output, before a folded combine writes its
+// kept rows): work-group b of the launch (b = x + y * gridDim.x, over every K
+// slice) zeroes rows b, b + nb, ... after its K loop, in 16-byte stores.
+__device__ inline void zero_rows_share(const GemmParams& p) {
+  const int nb = gridDim.x * gridDim.y, b = blockIdx.y * gridDim.x + blockIdx.x;
+  const int vecs = p.zero_N * p.zero_esz / 16;   // 16-byte vectors per row (N % 8 == 0)
+  for (int t = b; t < p.zero_T; t += nb) {
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.zero_y) + (long long)t * p.zero_N * p.zero_esz);
+    for (int c = threadIdx.x; c < vecs; c += blockDim.x) dst[c] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -274,7 +320,10 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 
   // ---- which tile
   int seg, nt, mt, r0, r1;
-  if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) return;
+  if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) {
+    if (p.zero_y) zero_rows_share(p);
+    return;
+  }
   const int m0 = r0 + mt * BM;        // first row-space row of the tile
   const bool extra = seg == p.nseg;   // the extra segment: its own operands, rows index A2 directly
 
@@ -283,6 +332,9 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   const int wave = tid >> 6;
   const int wave_n = wave % WN;
   const int wave_m = wave / WN;
+  int ftok[TM];
+  float fw[TM];
+  fold_prefetch<TM>(p, EPI == EPI_F32 && p.fold_y && !extra, m0 + wave_m * TM * 16, r1, lane, ftok, fw);
 
   // ---- per-thread global source rows. LDS layout: row r of a stage holds its 128
   // bytes of K as eight 16-byte columns, column c stored at position c ^ (r & 7),
@@ -458,17 +510,20 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #undef GEMM_LSTORE
 #undef GEMM_MATH
 #undef GEMM_SB
+  if (p.zero_y) zero_rows_share(p);
 
   if constexpr (std::is_same<BiasT, float>::value) {
     if (p.ksplit > 1) {   // partial sums of this slice; the bias goes with slice 0
       GemmParams q = p;
       q.C = reinterpret_cast<float*>(p.C) + (long long)blockIdx.y * p.c_split;
       if (blockIdx.y != 0) q.bias = nullptr;
-      gemm_epilogue<DT, EPI, BiasT, TN, TM>(q, acc, seg, nt * BN + wave_n * TN * 16, m0 + wave_m * TM * 16, r1, lane);
+      gemm_epilogue<DT, EPI, BiasT, TN, TM>(q, acc, seg, nt * BN + wave_n * TN * 16, m0 + wave_m * TM * 16, r1, lane,
+                                            ftok, fw);
       return;
     }
   }
-  gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + wave_m * TM * 16, r1, lane);
+  gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + wave_m * TM * 16, r1, lane, ftok,
+                                        fw);
 }
 
 
@@ -508,6 +563,10 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_n = wave % WN;
   const int g = wave / WN;
+  const bool fold = EPI == EPI_F32 && p.fold_y && !extra;
+  int ftok[TM];
+  float fw[TM];
+  fold_prefetch<TM>(p, fold, m0 + g * TM * 16, r1, lane, ftok, fw);
 
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(extra ? p.A2 : p.A);
   const char* bbase = extra    ? reinterpret_cast<const char*>(p.B2)
@@ -646,7 +705,10 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
 #undef DM_FRAGS
 #undef DM_MATH
 #undef DM_BAR
-  if constexpr (EPI != EPI_GELU || sizeof(T) == 2) {
+  if (fold) {
+    gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + g * TM * 16, r1, lane, ftok,
+                                          fw);
+  } else if constexpr (EPI != EPI_GELU || sizeof(T) == 2) {
     // every wave is past its last fragment read of the K loop's buffers before
     // any wave overwrites them with its output rows (8 x 16 TM rows of 128 B)
     static_assert(8 * TM * 16 * 128 <= 3 * STAGE, "output blocks fit the K-step buffers");
@@ -654,7 +716,8 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
     gemm_epilogue_lds<DT, EPI, BiasT, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + g * TM * 16, r1, lane,
                                           smem + wave * (TM * 16 * 128));
   } else {
-    gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + g * TM * 16, r1, lane);
+    gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + g * TM * 16, r1, lane, ftok,
+                                          fw);
   }
 }
 

@@ -109,7 +109,8 @@ struct Plan {
   int nblk;
   // experts
   bool exp_decode;   // streaming kernels for segments of <= 8 rows, else grouped MFMA GEMM
-  bool fold_combine; // top-1 standard layer on the decode path: the expert kernel writes y
+  bool fold_combine; // top-1 standard layer: the second expert kernel (decode or grouped GEMM) writes y
+  bool zero_in_gate; // with fold_combine: the matrix-core gate zeroes y first
   bool route_in_up;  // decode path with a tiny batch: the first expert kernel does the dispatch
   bool fused_decode; // ... and both expert products run in one launch (h marked unwritten by the gate)
   int exp_maxm;
@@ -203,7 +204,13 @@ moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl) {
   const int64_t seg_rows = std::min<int64_t>(p.C, kT);
   p.exp_maxm = pow2_at_least(std::max<int64_t>(seg_rows, 1));
   p.exp_decode = seg_rows <= 8 && decode_supported(p.dtype, p.H, p.F);
-  p.fold_combine = p.exp_decode && p.k == 1 && !p.residual;
+  // top-1 standard layers: the second expert kernel writes y itself (the decode
+  // kernel or the second grouped GEMM's epilogue)
+  p.fold_combine = p.k == 1 && !p.residual && p.R_max > 0;
+  // ... and the rows of tokens without a kept choice are zeroed: by the
+  // matrix-core gate's work-groups (all of y, before the dispatch) on the
+  // grouped-GEMM path, else by the routing (its dispatch or the decode kernel)
+  p.zero_in_gate = p.fold_combine && !p.exp_decode && p.gate_mfma;
   p.route_in_up = p.exp_decode && route_in_decode_supported((int)p.T, p.k, p.E, p.E_loc);
   // one launch for both expert products: the vector-ALU gate kernel marks its h rows unwritten
   p.fused_decode = (d->flags & MOE_FLAG_DECODE_ONE_LAUNCH) && p.route_in_up && !p.gate_mfma &&
@@ -372,10 +379,18 @@ moe_status_t check_weights(const Plan& p, const moe_layer_weights_t* w, bool exp
 }
 
 // ---------------------------------------------------------------- launch steps
+// y_zero (matrix-core gate only): the layer output, zeroed by the gate's
+// work-groups before a folded top-1 combine writes its kept rows.
 moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, const float* gate_b, float* z,
-                             hipStream_t s, unsigned* fill = nullptr, int nfill = 0) {
+                             hipStream_t s, unsigned* fill = nullptr, int nfill = 0, void* y_zero = nullptr) {
   if (p.gate_mfma) {
     GemmParams g{};
+    if (y_zero) {
+      g.zero_y = y_zero;
+      g.zero_T = (int)p.T;
+      g.zero_esz = (int)p.esz;
+      g.zero_N = p.H;
+    }
     g.A = x;
     g.M = (int)p.T;
     g.nseg = 1;
@@ -536,6 +551,11 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
   g2.n_ntiles = nt2;
   g2.stream_w = p.stream_w2 ? 1 : 0;
   g2.off32 = p.off32 ? 1 : 0;
+  if (y_fold) {   // top-1 combine in the epilogue
+    g2.fold_y = y_fold;
+    g2.fold_token = slot_token;
+    g2.fold_w = topk_w;
+  }
   if (dense) {   // m = h_dense W2_mlp^T + b2_mlp, fp32
     g2.A2 = wsp<void>(ws, p.o_dh);
     g2.B2 = w->mlp_w2;
@@ -782,7 +802,8 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   ST_TRY(record(e.gate_begin, stream));
   // the one-launch decode kernel finds its hidden rows marked unwritten (0xFFFF)
   ST_TRY(run_gate_logits(p, x, w->gate_w, w->gate_b, z, stream, p.fused_decode ? wsp<unsigned>(ws, p.o_h) : nullptr,
-                         p.fused_decode ? (int)(p.R_max * p.F * (int64_t)p.esz / 4) : 0));
+                         p.fused_decode ? (int)(p.R_max * p.F * (int64_t)p.esz / 4) : 0,
+                         p.zero_in_gate ? y : nullptr));
   ST_TRY(record(e.gate_end, stream));
   ST_TRY(record(e.dispatch_begin, stream));
   RouteParams rp{};
@@ -808,8 +829,8 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   } else {
     // the GEMM path's tile lists come out of the dispatch kernel that finds the offsets
     const TilePlanArgs tp = tile_plan_args(p, ws, true);
-    ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot, y_fold, ws, stream,
-                        p.exp_decode ? nullptr : &tp));
+    ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot,
+                        p.zero_in_gate ? nullptr : y_fold, ws, stream, p.exp_decode ? nullptr : &tp));
   }
   ST_TRY(record(e.dispatch_end, stream));
   ST_TRY(record(e.ffn_begin, stream));

@@ -68,6 +68,14 @@ CASES = {
     # edge cases: the maximum expert count (8 logits per lane in the top-k), a
     # ragged token count (gate token blocks of 8), heavy drops (cf = 0.1), one
     # token through a residual layer, and a share of a single local expert
+    # top-1 layers whose combine runs in the second GEMM's epilogue on the
+    # ping-pong tiles (segments > 64 rows), one with non-local tokens to zero
+    "gemm_pp_fold": W.LayerShape("gppf", T=2048, H=256, F=512, E=8, E_loc=8, k=1, cf=1.0, dtype="f16"),
+    "gemm_pp_fold_share_bf16": W.LayerShape("gppfs", T=1500, H=512, F=768, E=8, E_loc=3, e_lo=4, k=1, cf=1.25,
+                                            dtype="bf16"),
+    # one local expert of 64: four tiles in the first GEMM, whose work-groups zero
+    # ~1000 dropped / non-local tokens' rows each
+    "gemm_fold_few_tiles": W.LayerShape("gfft", T=4096, H=256, F=512, E=64, E_loc=1, k=1, cf=1.0, dtype="f16"),
     "e512_decode": W.LayerShape("e512d", T=8, H=512, F=512, E=512, E_loc=512, k=2, cf=1.0, dtype="f16"),
     "e512_gemm": W.LayerShape("e512g", T=600, H=256, F=512, E=512, E_loc=512, k=1, cf=4.0, dtype="f16"),
     "ragged_t13": W.LayerShape("t13", T=13, H=512, F=1024, E=16, E_loc=16, k=2, cf=1.0, dtype="f16"),
@@ -268,6 +276,33 @@ def test_local_shares_sum_to_full_layer():
         acc += B.MoELayer(sh, ws_).forward(x).float()
     torch.cuda.synchronize()
     G.assert_close(G.host(acc), G.host(yf), "f16", "sum of 4 shares vs full layer")
+
+
+@pytest.mark.parametrize("dtype,E,gate", [("f16", 16, "vector"), ("bf16", 16, "vector"), ("f16", 64, "matrix"),
+                                          ("bf16", 64, "matrix")])
+def test_folded_combine_without_kept_rows(dtype, E, gate):
+    """A top-1 layer whose local experts receive no token (the gate bias sends
+    every token to expert 0): neither grouped GEMM has a tile, and every row of
+    y (filled with 7s before) is still zeroed, by the dispatch (vector-ALU gate)
+    or by the matrix-core gate's work-groups, which is the oracle's combine for
+    tokens without a kept local choice."""
+    shape = W.LayerShape("nokept", T=300, H=256, F=512, E=E, E_loc=2, e_lo=8, k=1, cf=2.0, dtype=dtype)
+    G.say(f"[no kept rows] {dtype} E={E}")
+    plan = B.moe_layer_plan(B.desc_from_shape(shape))
+    assert plan["expert_path"] == "grouped_gemm" and plan["combine_in_expert_kernel"], plan
+    assert plan["gate_path"] == gate, plan
+    x, w = G.device_case(shape, seed=5)
+    w["gate_w"] = torch.zeros_like(w["gate_w"])
+    gb = torch.zeros(shape.E, dtype=torch.float32, device="cuda")
+    gb[0] = 4.0
+    w["gate_b"] = gb
+    hx, hw = G.host(x), G.host_weights(w)
+    route = oracle.route(hx, hw["gate_w"], hw["gate_b"], shape.k, False)
+    assert np.all(route["idx"] == 0)
+    y = torch.full_like(x, 7.0)
+    B.MoELayer(shape, w).forward(x, y)
+    torch.cuda.synchronize()
+    assert int((y != 0).sum()) == 0
 
 
 def test_dispatch_zero_tokens():
