@@ -169,6 +169,9 @@ def test_steps_and_layer_match_oracle(name):
     (5000, 512, 2, 512, 0, 1.0, False),   # multi-block with the largest expert count
     (16385, 8, 1, 8, 0, 1.0, True),       # seventeen blocks, the last holding one assignment
     (9000, 32, 2, 24, 4, 1.0, False),     # multi-block, local share, top-2
+    (4096, 64, 2, 64, 0, 1.0, True),      # eight blocks, top-2, hot expert
+    (8193, 8, 1, 8, 0, 1.0, False),       # nine blocks, the last holding one assignment
+    (2500, 128, 1, 16, 100, 1.25, True),  # local share near the top of the expert range
 ])
 def test_dispatch_fed_oracle_routing(T, E, k, E_loc, e_lo, cf, hot):
     G.say(f"[dispatch] T={T} E={E} k={k} E_loc={E_loc} e_lo={e_lo} cf={cf} hot={hot}")
