@@ -19,14 +19,18 @@
 // weight bandwidth) keep two stages of loads in flight in a register ping-pong,
 // 128 x 128 tiles one.
 //
-// grouped_gemm_pp_kernel: the eight-wave 128 x 256 and 160 x 256 tiles of long
-// segments and the dense MLP. With all eight waves in the same phase of a K
-// step, the LDS reads and the MFMAs of a step ran one after the other; there the
-// two halves of the work-group run half a step apart, and the K steps reach
-// three LDS buffers (same swizzled layout) by direct-to-LDS buffer loads.
+// grouped_gemm_pp_kernel: the eight-wave 128 x 256 tiles of long segments and
+// the dense MLP. With all eight waves in the same phase of a K step, the LDS
+// reads and the MFMAs of a step ran one after the other; there the two halves
+// of the work-group run half a step apart, and the K steps reach three LDS
+// buffers (same swizzled layout) by direct-to-LDS buffer loads.
+// grouped_gemm_pp320_kernel: the same schedule on 320 x 256 tiles (one per
+// segment of 257..320 rows) with 80 x 128 wave blocks, two LDS stages and
+// sub-steps of 32 K.
 //
 // Epilogues: bias + exact GeLU rounded to the I/O dtype (first expert GEMM), or
-// bias in fp32 (second GEMM and gate logits).
+// bias in fp32 (second GEMM and gate logits); the ping-pong tiles stage their
+// output rows through LDS.
 //
 // Tiles come from a device tile list built on the device from the kept rows of
 // each segment, by the dispatch kernel that fills the segments or by the plan
@@ -532,16 +536,17 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #define MOE_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
 #define MOE_LGKM0 0xC07F
 
-// Eight-wave 256-column tiles (BM = 128 or 160) for long segments and the dense
-// MLP, where the matrix cores set the pace. Ping-pong schedule: waves 0-3 (the
+// Eight-wave 128 x 256 tiles for segments of 65..256 rows and the dense MLP,
+// where the matrix cores set the pace. Ping-pong schedule: waves 0-3 (the
 // tile's upper rows) and waves 4-7 (lower rows) run half a K step apart, so on
 // every SIMD one wave multiplies while the other reads its fragments of the next
 // step from LDS. The K steps reach LDS by direct-to-LDS buffer loads (no
 // registers, no LDS store instructions) into three buffers, issued two steps
 // ahead. Every wave passes 2 nk + 2 barriers. Measured on the 24B-share expert
-// GEMMs (16 experts, H = 8192, F = 32768, 160 x 256 tiles): 2.74 / 2.67 ms per
-// launch; 2.91 / 2.74 ms with the steps staged through registers and LDS
-// stores, 3.39 / 3.37 ms with all eight waves in the same phase.
+// GEMMs (16 experts, H = 8192, F = 32768) with this kernel at 160 x 256 (two
+// tiles per 320-row segment, before the 320 x 256 kernel took those): 2.74 /
+// 2.67 ms per launch; 2.91 / 2.74 ms with the steps staged through registers
+// and LDS stores, 3.39 / 3.37 ms with all eight waves in the same phase.
 template <typename DT, int BM, int EPI, typename BiasT, bool WNT>
 __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
   using T = typename DT::T;
@@ -549,10 +554,10 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
   constexpr int TN = 4, TM = BM / 32;
   constexpr int HB = BM / 2;
   constexpr int NCG = 16 + HB / 8;            // 8-row chunks of one group's half of a K step
-  constexpr int NCH = (NCG + 3) / 4;          // chunks per wave (the extras load into a dummy area)
+  constexpr int NCH = NCG / 4;                // chunks per wave
+  static_assert(NCH * 4 == NCG, "a group's chunks split evenly over its four waves");
   constexpr int STAGE = (BN + BM) * LDS_ROW;
-  constexpr int DUMMY = 3 * STAGE;
-  __shared__ __attribute__((aligned(16))) char smem[3 * STAGE + (NCH * 4 > NCG ? 1024 : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[3 * STAGE];
 
   int seg, nt, mt, r0, r1;
   if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) return;
@@ -573,8 +578,8 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
                       : p.Bp ? reinterpret_cast<const char*>(p.Bp[seg])
                              : reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
   const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(bbase + (long long)nt * BN * p.K * (long long)sizeof(T));
-  // chunk i of this wave: c = wave_n + 4 i; c < 16 weight rows 128 g + 8 c, c < NCG
-  // activation rows HB g + 8 (c - 16), else a dummy. A wave's LDS DMA writes
+  // chunk i of this wave: c = wave_n + 4 i; c < 16 weight rows 128 g + 8 c, else
+  // activation rows HB g + 8 (c - 16). A wave's LDS DMA writes
   // 64 x 16 bytes contiguously: lane l lands in row l / 8 of the chunk, 16-byte
   // slot l % 8, so it loads column (l % 8) ^ (l / 8) (the XOR swizzle).
   const int col = ((lane & 7) ^ (lane >> 3)) * 16;
@@ -587,19 +592,12 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
       const int row = g * 128 + c * 8 + (lane >> 3);
       voff[i] = (unsigned)(row * p.K * (int)sizeof(T)) + col;
       ldst[i] = (g * 128 + c * 8) * LDS_ROW;
-    } else if (c < NCG) {
+    } else {
       int r = m0 + g * HB + (c - 16) * 8 + (lane >> 3);
       if (r >= r1) r = r1 - 1;
       const long long arow = (p.a_rows && !extra) ? (long long)p.a_rows[r] : (long long)r;
       voff[i] = (unsigned)(arow * p.K * (long long)sizeof(T)) + col;
       ldst[i] = BN * LDS_ROW + (g * HB + (c - 16) * 8) * LDS_ROW;
-    } else {
-      // a spare chunk (160-row tiles: 28 chunk slots for 26 chunks) repeats this
-      // wave's first activation chunk (i == 4, always a real one, its row clamped
-      // into the segment), since DM_ISSUE reads chunks i >= 4 through the
-      // activation descriptor; its data lands in the dummy LDS area
-      voff[i] = voff[4];
-      ldst[i] = -1;
     }
   }
 
@@ -620,11 +618,10 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc,                                   \
           (__attribute__((address_space(3))) void*)(smem + (BUF) * STAGE + ldst[i]), 16,  \
           (int)voff[i], (KS) * 128, 0, W_ ? MOE_CPOL_NT : 0);                            \
-    _Pragma("unroll") for (int i = 4; i < NCH; ++i) {                                    \
-      char* dst_ = ldst[i] < 0 ? smem + DUMMY : smem + (BUF) * STAGE + ldst[i];          \
+    _Pragma("unroll") for (int i = 4; i < NCH; ++i)                                      \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc,                                   \
-          (__attribute__((address_space(3))) void*)dst_, 16, (int)voff[i], (KS) * 128, 0, 0); \
-    }                                                                                    \
+          (__attribute__((address_space(3))) void*)(smem + (BUF) * STAGE + ldst[i]), 16,  \
+          (int)voff[i], (KS) * 128, 0, 0);                                               \
   }
 #define DM_FRAGS(BUF)                                                                    \
   {                                                                                      \
@@ -721,6 +718,184 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
   }
 }
 
+// Eight-wave 320 x 256 tiles for segments of 257..320 rows (the expert GEMMs of
+// a capacity-320 share): one work-group covers a whole segment, so each weight
+// tile is read once, and each wave holds an 80 x 128 block (160 accumulator
+// VGPRs), which reads 28 % fewer LDS fragment bytes per multiply than the
+// 80 x 64 blocks of the 160 x 256 tiles. Two LDS stages of 73.7 KB (256 weight
+// rows and 320 activation rows of 128 bytes of K, same swizzle) in two separate
+// arrays, so that the compiler sees which stage a direct-to-LDS load writes and
+// which one a fragment read reads, and adds no wait of its own between them.
+// Waves 0-3 (rows 0-159) and 4-7 (rows 160-319) run half a phase apart on
+// sub-steps of 32 K (one sub-step's fragments, 52 VGPRs, fit beside the
+// accumulators): on every SIMD one wave multiplies while the other reads its
+// fragments. Each group loads its half of a stage (its 160 activation rows and
+// 128 of the weight rows) in its memory phase of sub-step 2 s, after the
+// barrier that frees the buffer, and waits for its loads (vmcnt 0) right before
+// the barrier after which stage s + 1 is first read: group 0 at the end of its
+// multiply phase of sub-step 2 s + 1, group 1 at the end of its memory phase
+// of that sub-step (3.5 and 2.5 phases after the issue). No load is then in
+// flight at the loop's back edge, where the compiler waits for all of them.
+template <typename DT, int EPI, typename BiasT, bool WNT>
+__global__ __launch_bounds__(512, 2) void grouped_gemm_pp320_kernel(GemmParams p) {
+  using T = typename DT::T;
+  constexpr int BM = 320, BN = 256;
+  constexpr int TN = 8, TM = 5;
+  constexpr int NCH = 9;                       // 8-row chunks per wave per stage: (16 + 20) per group / 4
+  constexpr int STAGE = (BN + BM) * LDS_ROW;
+  __shared__ __attribute__((aligned(16))) char lds0[STAGE];
+  __shared__ __attribute__((aligned(16))) char lds1[STAGE];
+
+  int seg, nt, mt, r0, r1;
+  if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) return;
+  const int m0 = r0 + mt * BM;
+  const bool extra = seg == p.nseg;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2;          // row half: activation rows 160 g ..
+  const int wm = (wave >> 1) & 1;   // 80-row block within the half
+  const int wn = wave & 1;          // 128-column block
+  const int wl = wave & 3;          // wave within its group (load chunks)
+  const int mw = m0 + g * 160 + wm * 80;   // first row of this wave's block
+  const bool fold = EPI == EPI_F32 && p.fold_y && !extra;
+  int ftok[TM];
+  float fw[TM];
+  fold_prefetch<TM>(p, fold, mw, r1, lane, ftok, fw);
+
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(extra ? p.A2 : p.A);
+  const char* bbase = extra    ? reinterpret_cast<const char*>(p.B2)
+                      : p.Bp ? reinterpret_cast<const char*>(p.Bp[seg])
+                             : reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(bbase + (long long)nt * BN * p.K * (long long)sizeof(T));
+  // chunk i of this wave: c = wl + 4 i; c < 16: weight rows 128 g + 8 c; else
+  // activation rows 160 g + 8 (c - 16) (clamped into the segment). Lane l lands
+  // in row l / 8 of the chunk, 16-byte slot l % 8, so it loads column
+  // (l % 8) ^ (l / 8) (the XOR swizzle).
+  const int col = ((lane & 7) ^ (lane >> 3)) * 16;
+  unsigned voff[NCH];
+  int ldst[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = wl + 4 * i;
+    if (i < 4) {
+      const int row = g * 128 + c * 8 + (lane >> 3);
+      voff[i] = (unsigned)(row * p.K * (int)sizeof(T)) + col;
+      ldst[i] = (g * 128 + c * 8) * LDS_ROW;
+    } else {
+      int r = m0 + g * 160 + (c - 16) * 8 + (lane >> 3);
+      if (r >= r1) r = r1 - 1;
+      const long long arow = (p.a_rows && !extra) ? (long long)p.a_rows[r] : (long long)r;
+      voff[i] = (unsigned)(arow * p.K * (long long)sizeof(T)) + col;
+      ldst[i] = BN * LDS_ROW + (g * 160 + (c - 16) * 8) * LDS_ROW;
+    }
+  }
+
+  float4_t acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (int)(((long long)p.K * sizeof(T)) / 128);
+  const int frag_row = lane & 15;
+  const int frag_c0 = (((lane >> 4)) ^ (frag_row & 7)) * 16;
+  const int frag_c1 = ((4 + (lane >> 4)) ^ (frag_row & 7)) * 16;
+
+#define P3_ISSUE(KS, BUF)                                                                \
+  {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc,                                   \
+          (__attribute__((address_space(3))) void*)((BUF) + ldst[i]), 16, (int)voff[i],  \
+          (KS) * 128, 0, W_ ? MOE_CPOL_NT : 0);                                          \
+    _Pragma("unroll") for (int i = 4; i < NCH; ++i)                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc,                                   \
+          (__attribute__((address_space(3))) void*)((BUF) + ldst[i]), 16, (int)voff[i],  \
+          (KS) * 128, 0, 0);                                                             \
+  }
+#define P3_FRAGS(BUF, KB)                                                                \
+  {                                                                                      \
+    const int fc_ = (KB) ? frag_c1 : frag_c0;                                            \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                       \
+      fa[i] = *reinterpret_cast<const uint4*>((BUF) + (wn * 128 + i * 16 + frag_row) * LDS_ROW + fc_); \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j)                                       \
+      fb[j] = *reinterpret_cast<const uint4*>((BUF) + (BN + g * 160 + wm * 80 + j * 16 + frag_row) * LDS_ROW + fc_); \
+  }
+#define P3_MATH                                                                          \
+  {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                       \
+      _Pragma("unroll") for (int j = 0; j < TM; ++j)                                     \
+        acc[i][j] = Mfma<DT>::op(fa[i], fb[j], acc[i][j]);                               \
+  }
+#define P3_BAR                                                                           \
+  {                                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                   \
+    asm volatile("" ::: "memory");                                                       \
+    __builtin_amdgcn_s_barrier();                                                        \
+    asm volatile("" ::: "memory");                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                   \
+  }
+// one sub-step (stage S, K half KB) read from BUF; NBUF is the other stage
+#define P3_SUB(S, KB, BUF, NBUF)                                                         \
+  {                                                                                      \
+    P3_FRAGS(BUF, KB);                                                                   \
+    if ((KB) == 0 && (S) + 1 < nk) P3_ISSUE((S) + 1, NBUF);                              \
+    if (g == 1 && (KB) == 1 && (S) + 1 < nk) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));   \
+    __builtin_amdgcn_s_waitcnt(MOE_LGKM0);                                               \
+    P3_BAR;                                                                              \
+    P3_MATH;                                                                             \
+    if (g == 0 && (KB) == 1 && (S) + 1 < nk) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));   \
+    P3_BAR;                                                                              \
+  }
+
+  auto k_loop = [&](auto stream_tag) {
+    constexpr bool W_ = decltype(stream_tag)::value;
+    uint4 fa[TN], fb[TM];
+    // stage 0 (both groups' halves) complete before the first barrier
+    P3_ISSUE(0, lds0);
+    __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+    P3_BAR;
+    if (g == 1) P3_BAR;
+    for (int s = 0; s < nk; s += 2) {
+      P3_SUB(s, 0, lds0, lds1);
+      P3_SUB(s, 1, lds0, lds1);
+      if (s + 1 < nk) {
+        P3_SUB(s + 1, 0, lds1, lds0);
+        P3_SUB(s + 1, 1, lds1, lds0);
+      }
+    }
+    if (g == 0) P3_BAR;
+  };
+  if constexpr (WNT) {
+    if (extra) k_loop(std::false_type{});
+    else k_loop(std::true_type{});
+  } else {
+    k_loop(std::false_type{});
+  }
+#undef P3_ISSUE
+#undef P3_FRAGS
+#undef P3_MATH
+#undef P3_BAR
+#undef P3_SUB
+  const int n0 = nt * BN + wn * 128;
+  if (fold) {
+    gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, n0, mw, r1, lane, ftok, fw);
+  } else if constexpr (EPI != EPI_GELU || sizeof(T) == 2) {
+    // every wave is past its last fragment read before any wave overwrites the
+    // stages with its output rows (waves 0-3 in the first array, 4-7 in the
+    // second, 16 TM rows of 128 bytes each), 64 columns at a time
+    static_assert(4 * TM * 16 * 128 <= STAGE, "output blocks fit a stage");
+    __syncthreads();
+    char* area = (g == 0 ? lds0 : lds1) + wl * (TM * 16 * 128);
+    gemm_epilogue_lds<DT, EPI, BiasT, TM>(p, reinterpret_cast<const float4_t(&)[4][TM]>(acc[0]), seg, n0, mw, r1,
+                                          lane, area);
+    gemm_epilogue_lds<DT, EPI, BiasT, TM>(p, reinterpret_cast<const float4_t(&)[4][TM]>(acc[4]), seg, n0 + 64, mw,
+                                          r1, lane, area);
+  } else {
+    gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, n0, mw, r1, lane, ftok, fw);
+  }
+}
+
 // ---------------------------------------------------------------- plan kernel
 // Tile lists of the two expert GEMMs from the segment offsets (one block; the
 // layer forward builds them inside its dispatch kernel instead).
@@ -755,10 +930,17 @@ static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) 
     // (launch_grouped_gemm refuses float-bias 256-column tiles and operands
     // beyond 32-bit offsets before getting here)
     if constexpr (!std::is_same<BiasT, float>::value) {
-      if (p.stream_w)
-        MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
-      else
-        MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+      if constexpr (BM == 320) {
+        if (p.stream_w)
+          MOE_LAUNCH((grouped_gemm_pp320_kernel<DT, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+        else
+          MOE_LAUNCH((grouped_gemm_pp320_kernel<DT, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+      } else {
+        if (p.stream_w)
+          MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+        else
+          MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+      }
     }
   } else {
     // (float bias: the gate's logits, whose weight tile every token tile reads)
@@ -793,12 +975,12 @@ static bool launch_bm(int BM, int epi, bool bias_f32, const GemmParams& p, int g
   return false;
 }
 
-// 128 x 256 and 160 x 256 tiles, eight waves: segments of 65..320 rows and the dense MLP
+// 128 x 256, 160 x 256 and 320 x 256 tiles, eight waves: segments of 65..320 rows and the dense MLP
 template <typename DT>
 static bool launch_big(int BM, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   switch (BM) {
     case 128: launch_epi<DT, 128, 256>(epi, bias_f32, p, grid, s, ev); return true;
-    case 160: launch_epi<DT, 160, 256>(epi, bias_f32, p, grid, s, ev); return true;
+    case 320: launch_epi<DT, 320, 256>(epi, bias_f32, p, grid, s, ev); return true;
   }
   return false;
 }

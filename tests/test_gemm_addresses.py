@@ -1,12 +1,12 @@
 """Address bounds of the ping-pong grouped GEMM's direct-to-LDS loads (CPU only).
 
-The eight-wave 128 x 256 / 160 x 256 tiles load each K step through two buffer
+The eight-wave 128 x 256 / 320 x 256 tiles load each K step through two buffer
 descriptors without range checks: the weight descriptor starts at the tile's
 first weight row, the activation descriptor at row 0 of the activation matrix.
 This replays the kernel's per-lane offset formulas for every wave, lane and
 chunk of a tile and checks that every 16-byte read of every K step stays inside
 its matrix, for the tile shapes the layer plan picks, including tiles taller
-than the whole batch (the 160-row tile of a 150-token top-2 layer)."""
+than the whole batch (the 320-row tile of a 150-token top-2 layer)."""
 import pytest
 
 from mixture_experts_transformer_moe_amd import binding as B
@@ -15,10 +15,11 @@ from mixture_experts_transformer_moe_amd import binding as B
 def pp_offsets(BM, K, esz, m0, r1, a_rows=None):
     """(descriptor, byte offset) of every chunk load of every lane, as the kernel
     computes them: chunks i < 4 are weight rows, the rest activation rows
-    (clamped into the segment), spare chunk slots repeat chunk 4."""
+    (clamped into the segment)."""
     HB = BM // 2
     NCG = 16 + HB // 8
-    NCH = (NCG + 3) // 4
+    NCH = NCG // 4
+    assert NCH * 4 == NCG
     out = []
     for wave in range(8):
         wave_n, g = wave % 4, wave // 4
@@ -30,20 +31,54 @@ def pp_offsets(BM, K, esz, m0, r1, a_rows=None):
                 if i < 4:
                     row = g * 128 + c * 8 + (lane >> 3)
                     voff.append(("w", row * K * esz + col))
-                elif c < NCG:
+                else:
                     r = min(m0 + g * HB + (c - 16) * 8 + (lane >> 3), r1 - 1)
                     arow = a_rows[r] if a_rows is not None else r
                     voff.append(("a", arow * K * esz + col))
-                else:
-                    voff.append(("a", voff[4][1]))
             out.extend(voff)
     return out
+
+
+def pp320_offsets(K, esz, m0, r1, a_rows=None):
+    """The same for the 320 x 256 tiles: each group (waves 0-3, 4-7) loads 128
+    weight rows and its 160 activation rows per stage, nine 8-row chunks per
+    wave (chunk c = wave % 4 + 4 i: c < 16 weight rows 128 g + 8 c, else
+    activation rows 160 g + 8 (c - 16), clamped into the segment)."""
+    out = []
+    for wave in range(8):
+        g, wl = wave // 4, wave % 4
+        for lane in range(64):
+            col = ((lane & 7) ^ (lane >> 3)) * 16
+            for i in range(9):
+                c = wl + 4 * i
+                if i < 4:
+                    row = g * 128 + c * 8 + (lane >> 3)
+                    out.append(("w", row * K * esz + col))
+                else:
+                    r = min(m0 + g * 160 + (c - 16) * 8 + (lane >> 3), r1 - 1)
+                    arow = a_rows[r] if a_rows is not None else r
+                    out.append(("a", arow * K * esz + col))
+    return out
+
+
+def pp320_lds_rows():
+    """LDS rows each wave's chunks land in (weights 0-255, activations 256-575):
+    every row of a stage exactly once."""
+    rows = []
+    for wave in range(8):
+        g, wl = wave // 4, wave % 4
+        for i in range(9):
+            c = wl + 4 * i
+            base = g * 128 + c * 8 if i < 4 else 256 + g * 160 + (c - 16) * 8
+            rows.extend(range(base, base + 8))
+    return rows
 
 
 def check_tile(BM, K, esz, m0, r1, a_total_rows, a_rows=None):
     nk = K * esz // 128
     last = (nk - 1) * 128 + 16          # the last step's 16 bytes past the base offset
-    for kind, off in pp_offsets(BM, K, esz, m0, r1, a_rows):
+    offs = pp320_offsets(K, esz, m0, r1, a_rows) if BM == 320 else pp_offsets(BM, K, esz, m0, r1, a_rows)
+    for kind, off in offs:
         assert off >= 0
         if kind == "w":
             assert off + last <= 256 * K * esz, (BM, kind, off)
@@ -51,7 +86,7 @@ def check_tile(BM, K, esz, m0, r1, a_total_rows, a_rows=None):
             assert off + last <= a_total_rows * K * esz, (BM, kind, off, a_total_rows)
 
 
-@pytest.mark.parametrize("BM", [128, 160])
+@pytest.mark.parametrize("BM", [128, 320])
 def test_expert_tiles_stay_inside_operands(BM):
     # first GEMM: A = x [T, H] read through slot_token; second GEMM: A = h [R_max, F]
     for T, H, seg in [(150, 256, 150), (1024, 512, 300), (20, 512, 17), (129, 256, 129)]:
@@ -63,15 +98,21 @@ def test_expert_tiles_stay_inside_operands(BM):
                 check_tile(BM, H, 2, r0 + mt * BM, r1, r1)       # h rows
 
 
-@pytest.mark.parametrize("BM", [128, 160])
+@pytest.mark.parametrize("BM", [128, 320])
 def test_dense_mlp_tiles_stay_inside_x(BM):
     for T in (1, 100, 150, 160, 300):
         for mt in range((T + BM - 1) // BM):
             check_tile(BM, 512, 2, mt * BM, T, T)
 
 
-def test_plan_picks_160_rows_for_short_batches():
-    """The layer plan does send a 150-token top-2 layer to 160-row tiles, so the
-    bound above is what keeps its loads inside x."""
+def test_pp320_stage_rows_each_loaded_once():
+    rows = pp320_lds_rows()
+    assert sorted(rows) == list(range(576))
+
+
+def test_plan_picks_320_rows_for_short_batches():
+    """The layer plan does send a 150-token top-2 layer to 320-row tiles (one
+    tile per 300-row segment), so the bound above is what keeps its loads
+    inside x."""
     plan = B.moe_layer_plan(B.make_desc(150, 256, 512, 2, 2, 2.0, "f16"))
-    assert plan["tile"] == (160, 256, 256)
+    assert plan["tile"] == (320, 256, 256)

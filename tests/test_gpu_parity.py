@@ -42,32 +42,34 @@ CASES = {
     "gemm_bn64": W.LayerShape("gbn64", T=256, H=320, F=512, E=16, E_loc=16, k=1, cf=1.0, dtype="f16"),
     "gemm_bf16_bm32": W.LayerShape("gbf", T=512, H=512, F=1024, E=16, E_loc=16, k=1, cf=1.0, dtype="bf16"),
     "gemm_bm64_k2": W.LayerShape("gk2", T=512, H=512, F=768, E=32, E_loc=32, k=2, cf=2.0, dtype="f16"),
-    # eight-wave 160 x 256 tiles: segments of up to C = 320 rows, two m-tiles each
-    "gemm_bm160": W.LayerShape("g160", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
-    "gemm_bm160_bf16_share": W.LayerShape("g160b", T=1024, H=512, F=1024, E=8, E_loc=4, e_lo=2, k=2, cf=1.25,
+    # eight-wave 320 x 256 tiles: segments of up to C = 320 rows, one m-tile each
+    "gemm_bm320": W.LayerShape("g160", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
+    "gemm_bm320_bf16_share": W.LayerShape("g160b", T=1024, H=512, F=1024, E=8, E_loc=4, e_lo=2, k=2, cf=1.25,
                                           dtype="bf16"),
-    # 160 x 256 tiles with the dense MLP's tiles in the same launches: expert
+    # 320 x 256 tiles with the dense MLP's tiles in the same launches: expert
     # weights streamed, the MLP's cached (two copies of the K loop)
-    "residual_bm160": W.LayerShape("r160", T=1024, H=512, F=1024, E=4, E_loc=4, k=1, cf=1.25, dtype="f16",
+    "residual_bm320": W.LayerShape("r160", T=1024, H=512, F=1024, E=4, E_loc=4, k=1, cf=1.25, dtype="f16",
                                    mlp_type="residual"),
     # 128 x 256 ping-pong tiles: with the dense MLP's tiles in the same launches,
     # and in bf16 with top-2 (segments of up to C = 150 rows)
     "residual_bm128": W.LayerShape("r128", T=1024, H=512, F=1024, E=8, E_loc=8, k=1, cf=1.0, dtype="f16",
                                    mlp_type="residual"),
     "gemm_bm128_bf16_k2": W.LayerShape("g128b", T=600, H=256, F=512, E=8, E_loc=8, k=2, cf=1.0, dtype="bf16"),
-    # 160 x 256 tiles over a batch of fewer than 160 tokens (C = 300, segments of
-    # 150 rows): every activation load of the first GEMM, spare chunks included,
-    # must stay inside x's 150 rows
-    "gemm_bm160_t150": W.LayerShape("g160t", T=150, H=256, F=512, E=2, E_loc=2, k=2, cf=2.0, dtype="f16"),
-    # ping-pong tiles at widths that are multiples of 256 but not of 512: 160 x
+    # 320 x 256 tiles over a batch of fewer than 320 tokens (C = 300, segments of
+    # 150 rows): every activation load of the first GEMM must stay inside x's
+    # 150 rows
+    "gemm_bm320_t150": W.LayerShape("g160t", T=150, H=256, F=512, E=2, E_loc=2, k=2, cf=2.0, dtype="f16"),
+    # ping-pong tiles at widths that are multiples of 256 but not of 512: 320 x
     # 256 tiles of a 768-wide first product, and a residual layer with both
     # products and the dense MLP on 128 x 256 tiles (H = F = 768, bf16)
-    "gemm_bm160_bn256": W.LayerShape("g160n", T=1024, H=512, F=768, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
+    "gemm_bm320_f768": W.LayerShape("g160n", T=1024, H=512, F=768, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
     "residual_bm128_bn256": W.LayerShape("r128n", T=1024, H=768, F=768, E=8, E_loc=8, k=1, cf=1.0, dtype="bf16",
                                          mlp_type="residual"),
     # edge cases: the maximum expert count (8 logits per lane in the top-k), a
     # ragged token count (gate token blocks of 8), heavy drops (cf = 0.1), one
     # token through a residual layer, and a share of a single local expert
+    # top-1 layer of 320-row segments: the folded combine on the 320 x 256 tiles
+    "gemm_bm320_fold": W.LayerShape("g320f", T=2048, H=256, F=512, E=8, E_loc=8, k=1, cf=1.25, dtype="f16"),
     # top-1 layers whose combine runs in the second GEMM's epilogue on the
     # ping-pong tiles (segments > 64 rows), one with non-local tokens to zero
     "gemm_pp_fold": W.LayerShape("gppf", T=2048, H=256, F=512, E=8, E_loc=8, k=1, cf=1.0, dtype="f16"),
