@@ -271,6 +271,14 @@ moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl) {
   // streaming). With smaller expert tiles the MLP would run on tiles too thin
   // for its T rows (measured slower), so it keeps its own launches.
   p.dense_in_experts = p.residual && !p.exp_decode && !p.dense_decode && p.BM >= 64;
+  // weight-streaming tiles (<= 64 rows) of a second GEMM with long weight rows:
+  // 64-column tiles halve each work-group's share of the weights (F = 8192,
+  // fp16: 1 MB instead of 2 MB), so the work-groups left over when the tile
+  // count is just past a multiple of the resident ones (33 experts x 16 tiles =
+  // 528 against 512) finish sooner: prefill layer 425 -> 417 us. Not with the
+  // dense MLP's tiles in the launch, which lose more on 64-column tiles than
+  // the experts gain (residual layer 955 -> 1010 us).
+  if (!p.exp_decode && p.BM <= 64 && p.BN2 == 128 && !p.dense_in_experts && (int64_t)p.F * p.esz > 8192) p.BN2 = 64;
   // segments of at most two row tiles: each expert weight tile is read by one
   // or two work-groups, so the first GEMM streams the expert weights with
   // non-temporal loads (the dense MLP's tiles in the same launches, read by

@@ -133,7 +133,8 @@ def test_layer_plan_paths():
     assert not B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["prefill_1p3b_moe128"].with_(one_launch=True)))[
         "experts_one_launch"]
     # tiles: 64-row tiles for segments of <= 64 rows; 160 x 256 for the 24B share's 320-row segments
-    assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["prefill_1p3b_moe128"]))["tile"] == (64, 128, 128)
+    assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["prefill_1p3b_moe128"]))["tile"] == (64, 128, 64)
+    assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["prmoe_residual"]))["tile"] == (64, 128, 128)
     assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["share_24b_moe128"]))["tile"] == (320, 256, 256)
     assert B.moe_layer_plan(B.make_desc(1024, 768, 768, 8, 1, 1.0, "f16"))["tile"] == (128, 256, 256)
     assert B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["decode_350m_moe128"]))["tile"] == (0, 0, 0)

@@ -39,6 +39,8 @@ CASES = {
                                     dtype="f16"),
     # grouped GEMM with two stages in flight (tiles of <= 64 rows): 64-wide column
     # tiles (H = 320), bf16, and full 64-row tiles with top-2
+    # second GEMM with long weight rows (F = 8192): 64-column tiles by the plan
+    "gemm_long_f_bn64": W.LayerShape("glf", T=512, H=256, F=8192, E=16, E_loc=16, k=1, cf=1.25, dtype="f16"),
     "gemm_bn64": W.LayerShape("gbn64", T=256, H=320, F=512, E=16, E_loc=16, k=1, cf=1.0, dtype="f16"),
     "gemm_bf16_bm32": W.LayerShape("gbf", T=512, H=512, F=1024, E=16, E_loc=16, k=1, cf=1.0, dtype="bf16"),
     "gemm_bm64_k2": W.LayerShape("gk2", T=512, H=512, F=768, E=32, E_loc=32, k=2, cf=2.0, dtype="f16"),
