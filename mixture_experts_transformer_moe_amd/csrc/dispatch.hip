@@ -36,21 +36,26 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_count_kernel(const int* _
 }
 
 // Column scan of the block histograms (becomes each block's per-expert base),
-// demand, kept rows and the local segment offsets. One block.
+// demand, kept rows and the local segment offsets. One block. Each thread
+// loads eight blocks' counts of its expert at a time before it scans them.
 __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scan_kernel(int* __restrict__ blk_hist, int nblk,
                                                                    int E, int e_lo, int E_loc, int C,
                                                                    int* __restrict__ demand,
-                                                                   int* __restrict__ offsets, TilePlanArgs plan) {
+                                                                   int* __restrict__ offsets) {
   __shared__ int sdem[1024];
   __shared__ int ssc[DISP_WAVES + 1];
-  __shared__ int plds[tile_plan_lds_ints(DISP_BLOCK)];
   const int tid = threadIdx.x;
   if (tid < E) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk_hist[(long long)b * E + tid];
-      blk_hist[(long long)b * E + tid] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = b0 + i < nblk ? blk_hist[(long long)(b0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (b0 + i < nblk) blk_hist[(long long)(b0 + i) * E + tid] = run;
+        run += c[i];
+      }
     }
     demand[tid] = run;
     sdem[tid] = run;
@@ -61,13 +66,23 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scan_kernel(int* __restri
   const int off = block_excl_scan<DISP_BLOCK>(kept, ssc, &total);
   if (tid < E_loc) offsets[tid] = off;
   if (tid == 0) offsets[E_loc] = total;
-  if (plan.list1 || plan.list2) tile_plan_body<DISP_BLOCK>(kept, E_loc, plan, plds);
 }
 
+// Slots of the assignments of block b < nblk; with tile lists to write, one
+// more block (past every assignment) builds them from the segment offsets
+// while the others scatter.
 __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
     const int* __restrict__ idx, const int* __restrict__ rank, const int* __restrict__ base, int T, int k,
     int E, int e_lo, int E_loc, int C, const int* __restrict__ offsets, int R_max,
-    int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H) {
+    int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H, int nblk,
+    TilePlanArgs plan) {
+  if ((int)blockIdx.x == nblk) {
+    __shared__ int plds[tile_plan_lds_ints(DISP_BLOCK)];
+    const int tid = threadIdx.x;
+    const int rows = tid < E_loc ? offsets[tid + 1] - offsets[tid] : 0;
+    tile_plan_body<DISP_BLOCK>(rows, E_loc, plan, plds);
+    return;
+  }
   const int kT = T * k;
   const int a = blockIdx.x * DISP_BLOCK + threadIdx.x;
   if (a < kT) {
@@ -86,7 +101,7 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
     if (y_zero && slot < 0) zero_dropped(y_zero, y_esz, t, H);
   }
   const int R = offsets[E_loc];
-  for (int s = R + blockIdx.x * DISP_BLOCK + threadIdx.x; s < R_max; s += gridDim.x * DISP_BLOCK)
+  for (int s = R + blockIdx.x * DISP_BLOCK + threadIdx.x; s < R_max; s += nblk * DISP_BLOCK)
     slot_token[s] = -1;
 }
 
@@ -237,11 +252,13 @@ hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(DISP_BLOCK), 0, s, blk_hist, nblk, E, e_lo, E_loc,
-                     C, demand, offsets, plan_or_none(plan));
+                     C, demand, offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(DISP_BLOCK), 0, s, idx, rank, blk_hist, T, k,
-                     E, e_lo, E_loc, C, offsets, R_max, slot_token, token_slot, y_zero, y_esz, H);
+  const TilePlanArgs pl = plan_or_none(plan);
+  const int extra = (pl.list1 || pl.list2) ? 1 : 0;   // the block that writes the tile lists
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk + extra), dim3(DISP_BLOCK), 0, s, idx, rank, blk_hist, T,
+                     k, E, e_lo, E_loc, C, offsets, R_max, slot_token, token_slot, y_zero, y_esz, H, nblk, pl);
   return hipGetLastError();
 }
 
