@@ -68,19 +68,19 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scan_kernel(int* __restri
   if (tid == 0) offsets[E_loc] = total;
 }
 
-// Slots of the assignments of block b < nblk; with tile lists to write, one
-// more block (past every assignment) builds them from the segment offsets
-// while the others scatter.
+// Slots of the assignments of block b < nblk; with tile lists to write, the
+// blocks past every assignment (nplan of them) build the lists from the segment
+// offsets while the others scatter.
 __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
     const int* __restrict__ idx, const int* __restrict__ rank, const int* __restrict__ base, int T, int k,
     int E, int e_lo, int E_loc, int C, const int* __restrict__ offsets, int R_max,
     int* __restrict__ slot_token, int* __restrict__ token_slot, void* y_zero, int y_esz, int H, int nblk,
-    TilePlanArgs plan) {
-  if ((int)blockIdx.x == nblk) {
+    int nplan, TilePlanArgs plan) {
+  if ((int)blockIdx.x >= nblk) {
     __shared__ int plds[tile_plan_lds_ints(DISP_BLOCK)];
     const int tid = threadIdx.x;
     const int rows = tid < E_loc ? offsets[tid + 1] - offsets[tid] : 0;
-    tile_plan_body<DISP_BLOCK>(rows, E_loc, plan, plds);
+    tile_plan_body<DISP_BLOCK>(rows, E_loc, plan, plds, (int)blockIdx.x - nblk, nplan);
     return;
   }
   const int kT = T * k;
@@ -256,9 +256,10 @@ hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, 
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const TilePlanArgs pl = plan_or_none(plan);
-  const int extra = (pl.list1 || pl.list2) ? 1 : 0;   // the block that writes the tile lists
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk + extra), dim3(DISP_BLOCK), 0, s, idx, rank, blk_hist, T,
-                     k, E, e_lo, E_loc, C, offsets, R_max, slot_token, token_slot, y_zero, y_esz, H, nblk, pl);
+  const int nplan = (pl.list1 || pl.list2) ? std::max(1, pl.parts) : 0;   // blocks that write the tile lists
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk + nplan), dim3(DISP_BLOCK), 0, s, idx, rank, blk_hist, T,
+                     k, E, e_lo, E_loc, C, offsets, R_max, slot_token, token_slot, y_zero, y_esz, H, nblk, nplan,
+                     pl);
   return hipGetLastError();
 }
 

@@ -454,6 +454,10 @@ TilePlanArgs tile_plan_args(const Plan& p, void* ws, bool with_dense) {
   a.n_nt1 = p.F / p.BN1;
   a.n_nt2 = p.H / p.BN2;
   a.mt_extra = (with_dense && p.dense_in_experts) ? p.mt_extra : 0;
+  // the multi-block dispatch builds the lists in blocks of about 2048 entries
+  // (their length bound: row tiles x column tiles of both GEMMs), at most 16
+  const int64_t bound = (int64_t)p.mt_bound * (a.n_nt1 + a.n_nt2);
+  a.parts = (int)std::min<int64_t>(16, std::max<int64_t>(1, (bound + 2047) / 2048));
   return a;
 }
 

@@ -15,6 +15,7 @@ struct TilePlanArgs {
   int BM;           // rows per tile
   int n_nt1, n_nt2; // column tiles of the two GEMMs
   int mt_extra;     // row tiles of the extra segment (id nseg), spread over the list
+  int parts;        // blocks that build the lists in the multi-block dispatch (>= 1)
 };
 
 // ints of LDS tile_plan_body<NTH> needs
@@ -23,9 +24,12 @@ __host__ __device__ constexpr int tile_plan_lds_ints(int nth) { return 2 * nth +
 // Thread s < nseg (nseg <= NTH) passes the rows of segment s. Expert tiles go
 // segment by segment, column tile, then row tile, so the row tiles that share a
 // weight tile are adjacent; the extra segment's tiles are spread evenly among
-// them. Every thread of the block must call it.
+// them. Every thread of the block must call it. With nparts blocks calling it,
+// block `part` writes list entries part * NTH + tid, ... (stride nparts * NTH)
+// and block 0 the count.
 template <int NTH>
-__device__ inline void tile_plan_body(int rows, int nseg, const TilePlanArgs& a, int* lds) {
+__device__ inline void tile_plan_body(int rows, int nseg, const TilePlanArgs& a, int* lds, int part = 0,
+                                      int nparts = 1) {
   constexpr int NW = NTH / 64;
   int* P = lds;              // [NTH + 1] first row tile of each segment
   int* C = P + NTH + 1;      // [NTH] row tiles of each segment
@@ -56,7 +60,7 @@ __device__ inline void tile_plan_body(int rows, int nseg, const TilePlanArgs& a,
   if (tid == 0) P[nseg] = wsum[NW];
   __syncthreads();
   const int total = wsum[NW];
-  if (tid == 0) a.count[0] = total + a.mt_extra;
+  if (tid == 0 && part == 0) a.count[0] = total + a.mt_extra;
   for (int g = 0; g < 2; ++g) {
     const int n_nt = g ? a.n_nt2 : a.n_nt1;
     int2* list = g ? a.list2 : a.list1;
@@ -68,7 +72,7 @@ __device__ inline void tile_plan_body(int rows, int nseg, const TilePlanArgs& a,
     // when its weights stay cached) with the expert tiles (weight streaming).
     const long long n_x = (long long)a.mt_extra * n_nt;
     const long long N = n_x + (long long)total * n_nt;
-    for (int L = tid; L < N; L += NTH) {
+    for (int L = part * NTH + tid; L < N; L += nparts * NTH) {   // (N < 2^31: checked by the plan)
       const long long cx = n_x ? ((long long)(L + 1) * n_x + N - 1) / N : 0;
       const long long cp = n_x ? ((long long)L * n_x + N - 1) / N : 0;
       if (cx > cp) {              // the extra segment's tile cx - 1: column tile major, then row tile
