@@ -295,7 +295,27 @@ __device__ inline int lds_load(const int* p) { return *(const __attribute__((add
 // Every small load a work-group's epilogue needs (activation row indices, bias,
 // the row's token and gate weight) is issued before or with the weight loads,
 // so only the weight stream itself is left to wait for.
-template <typename DT, int MAXM, int NQ>
+// KS waves share a block of weight rows, each taking 1 / KS of K (NQ vectors
+// per lane per row), and add their sums through LDS in wave order: rows longer
+// than 16 vectors per lane (K = 16384 or 32768 at 2-byte weights) keep the
+// registers and loads in flight of one wave at K = 8192.
+template <int KS, int NW>
+__device__ inline float ksplit_sum(float s, int wave, int lane, bool& keep) {
+  keep = true;
+  if constexpr (KS > 1) {
+    __shared__ float red[NW][64];
+    red[wave][lane] = s;
+    __syncthreads();
+    keep = (wave % KS) == 0;
+    float t = red[wave][lane];
+#pragma unroll
+    for (int i = 1; i < KS; ++i) t += red[wave + (keep ? i : 0)][lane];
+    return t;
+  }
+  return s;
+}
+
+template <typename DT, int MAXM, int NQ, int KS>
 __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(RouteParams rp, DecodeParams p) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
@@ -303,11 +323,12 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(RouteParams rp
   constexpr int SH = 6 - ilog2(N);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nchunk = p.F / (UP_WAVES * RPW);
+  const int nchunk = p.F / ((UP_WAVES / KS) * RPW);
   const int g = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - g * nchunk;
   const long long H = p.H, F = p.F;
-  const int f0 = chunk * UP_WAVES * RPW + wave * RPW;
+  const int f0 = chunk * (UP_WAVES / KS) * RPW + (wave / KS) * RPW;
+  const long long kofs = (long long)(wave % KS) * (H / KS);   // this wave's share of K
   // after the reduction lane l holds value v = l >> SH: weight row f0 + oi, activation row om
   const int v = lane >> SH;
   const int oi = v / MAXM, om = v - (v / MAXM) * MAXM;
@@ -324,7 +345,7 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(RouteParams rp
     if (e >= 0) {
       const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[e]) : reinterpret_cast<const T*>(p.w1) + (long long)e * F * H;
       const T* b1s = p.b1p ? reinterpret_cast<const T*>(p.b1p[e]) : reinterpret_cast<const T*>(p.b1) + (long long)e * F;
-      load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H, H);
+      load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H + kofs, H);
       bias_raw = gload(b1s + f0 + oi);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -348,22 +369,23 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(RouteParams rp
     const T* w1s = p.w1p ? reinterpret_cast<const T*>(p.w1p[seg]) : reinterpret_cast<const T*>(p.w1) + (long long)seg * F * H;
     const T* b1s = p.b1p ? reinterpret_cast<const T*>(p.b1p[seg]) : reinterpret_cast<const T*>(p.b1) + (long long)seg * F;
     bias_raw = gload(b1s + f0 + oi);
-    load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H, H);
+    load_rows<DT, NQ, RPW>(wv, w1s + (long long)f0 * H + kofs, H);
     __builtin_amdgcn_sched_barrier(0);   // every weight load is in flight before anything else
   }
   const int M = min(r1 - r0, MAXM);
   const T* x = reinterpret_cast<const T*>(p.x);
   const T* act[MAXM];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) act[m] = x + (long long)rows[m] * H;
-  const float s = dot_rows<DT, MAXM, NQ, RPW>(wv, act);
-  if ((lane & ((1 << SH) - 1)) == 0 && om < M) {
+  for (int m = 0; m < MAXM; ++m) act[m] = x + (long long)rows[m] * H + kofs;
+  bool keep;
+  const float s = ksplit_sum<KS, UP_WAVES>(dot_rows<DT, MAXM, NQ, RPW>(wv, act), wave, lane, keep);
+  if (keep && (lane & ((1 << SH) - 1)) == 0 && om < M) {
     const float u = s + DT::to_f(bias_raw);
     reinterpret_cast<T*>(p.h)[(long long)(r0 + om) * F + f0 + oi] = DT::from_f(pin_f32(gelu_erf(u)));
   }
 }
 
-template <typename DT, int MAXM, int NQ, bool FUSE>
+template <typename DT, int MAXM, int NQ, bool FUSE, int KS>
 __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodeParams p) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
@@ -371,7 +393,7 @@ __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodePara
   constexpr int SH = 6 - ilog2(N);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nchunk = p.H / (DOWN_WAVES * RPW);
+  const int nchunk = p.H / ((DOWN_WAVES / KS) * RPW);
   const int g = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - g * nchunk;
   int seg = 0, r0 = 0, r1 = p.M;
@@ -381,7 +403,8 @@ __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodePara
     return;
   }
   const long long H = p.H, F = p.F;
-  const int j0 = chunk * DOWN_WAVES * RPW + wave * RPW;
+  const int j0 = chunk * (DOWN_WAVES / KS) * RPW + (wave / KS) * RPW;
+  const long long kofs = (long long)(wave % KS) * (F / KS);   // this wave's share of K
   const int M = min(r1 - r0, MAXM);
   const int v = lane >> SH;
   const int oi = v / MAXM, om = v - (v / MAXM) * MAXM;
@@ -391,7 +414,7 @@ __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodePara
   if (FUSE) t_out = gload(p.slot_token + r0 + (om < M ? om : M - 1));   // a kept row: a token
   uint4 wv[RPW][NQ];
   const T* w2s = p.w2p ? reinterpret_cast<const T*>(p.w2p[seg]) : reinterpret_cast<const T*>(p.w2) + (long long)seg * H * F;
-  load_rows<DT, NQ, RPW>(wv, w2s + (long long)j0 * F, F);
+  load_rows<DT, NQ, RPW>(wv, w2s + (long long)j0 * F + kofs, F);
   __builtin_amdgcn_sched_barrier(0);
   float wt = 0.f;
   if (FUSE) {   // issued here, not after the dot: the token is back long before the weights
@@ -401,9 +424,10 @@ __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodePara
   const T* h = reinterpret_cast<const T*>(p.h);
   const T* act[MAXM];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) act[m] = h + (long long)(r0 + (m < M ? m : 0)) * F;
-  const float s = dot_rows<DT, MAXM, NQ, RPW>(wv, act);
-  if ((lane & ((1 << SH) - 1)) == 0 && om < M) {
+  for (int m = 0; m < MAXM; ++m) act[m] = h + (long long)(r0 + (m < M ? m : 0)) * F + kofs;
+  bool keep;
+  const float s = ksplit_sum<KS, DOWN_WAVES>(dot_rows<DT, MAXM, NQ, RPW>(wv, act), wave, lane, keep);
+  if (keep && (lane & ((1 << SH) - 1)) == 0 && om < M) {
     const float yv = s + DT::to_f(bias_raw);
     if (FUSE) {
       reinterpret_cast<T*>(p.out)[(long long)t_out * H + j0 + oi] = DT::from_f(pin_f32(fmaf(wt, yv, 0.f)));
@@ -668,35 +692,42 @@ struct LaunchEv {
   hipEvent_t start, stop;
 };
 
-template <typename DT, int MAXM, int NQ>
+template <typename DT, int MAXM, int NQ, int KS>
 static hipError_t launch_up_t(const DecodeParams& p, const RouteParams& rp, int grid_segs, hipStream_t s,
                               LaunchEv ev) {
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
-  const int grid = grid_segs * (p.F / (UP_WAVES * RPW));
+  const int grid = grid_segs * (p.F / ((UP_WAVES / KS) * RPW));
   const size_t lds = rp.z ? sizeof(int) * route_lds_ints(rp.T, rp.k, rp.R_max) : 0;
-  MOE_LAUNCH((decode_up_kernel<DT, MAXM, NQ>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start, ev.stop, rp, p);
+  MOE_LAUNCH((decode_up_kernel<DT, MAXM, NQ, KS>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start, ev.stop, rp,
+             p);
   return hipGetLastError();
 }
 
-template <typename DT, int MAXM, int NQ>
+template <typename DT, int MAXM, int NQ, int KS>
 static hipError_t launch_down_t(const DecodeParams& p, int grid_segs, bool fuse, hipStream_t s, LaunchEv ev) {
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
-  const int grid = grid_segs * (p.H / (DOWN_WAVES * RPW));
-  if (fuse) MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, true>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s, ev.start, ev.stop, p);
-  else MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, false>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s, ev.start, ev.stop, p);
+  const int grid = grid_segs * (p.H / ((DOWN_WAVES / KS) * RPW));
+  if (fuse)
+    MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, true, KS>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s, ev.start,
+               ev.stop, p);
+  else
+    MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, false, KS>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s, ev.start,
+               ev.stop, p);
   return hipGetLastError();
 }
 
+// K = 512 q at 2-byte weights: q <= 16 vectors per lane per row in one wave;
+// q = 32 / 64 split over 2 / 4 waves of 16 vectors each
 template <typename DT, int MAXM>
 static hipError_t launch_m(bool up, const DecodeParams& p, const RouteParams& rp, int grid_segs, bool fuse,
                            hipStream_t s, LaunchEv ev) {
   const int nq = up ? nq_of(p.H, DT::VEC) : nq_of(p.F, DT::VEC);
   switch (nq) {
-#define CASE(Q)                                                                                      \
+#define CASE(Q, NQ, KS)                                                                              \
   case Q:                                                                                            \
-    return up ? launch_up_t<DT, MAXM, Q>(p, rp, grid_segs, s, ev)                                    \
-              : launch_down_t<DT, MAXM, Q>(p, grid_segs, fuse, s, ev);
-    CASE(1) CASE(2) CASE(4) CASE(8) CASE(16)
+    return up ? launch_up_t<DT, MAXM, NQ, KS>(p, rp, grid_segs, s, ev)                               \
+              : launch_down_t<DT, MAXM, NQ, KS>(p, grid_segs, fuse, s, ev);
+    CASE(1, 1, 1) CASE(2, 2, 1) CASE(4, 4, 1) CASE(8, 8, 1) CASE(16, 16, 1) CASE(32, 16, 2) CASE(64, 16, 4)
 #undef CASE
   }
   return hipErrorInvalidValue;
@@ -779,9 +810,25 @@ bool decode_supported(int dtype, int H, int F) {
   auto ok = [](int K) {
     if (K % 512) return false;
     const int q = K / 512;
-    return q == 1 || q == 2 || q == 4 || q == 8 || q == 16;
+    return q == 1 || q == 2 || q == 4 || q == 8 || q == 16 || q == 32 || q == 64;
   };
   return ok(H) && ok(F);
+}
+
+// Work-groups of the larger of the two decode expert launches (groups_up /
+// groups_down segment groups): rows / (rows per work-group), with the K split
+// the row length asks for.
+long long decode_max_workgroups(int dtype, int H, int F, int maxm, long long groups_up, long long groups_down) {
+  const int vec = dtype == DT_F32 ? 4 : 8;
+  auto rows_per_wg = [&](int K, int waves) {
+    int nq = K / (64 * vec), ks = 1;
+    while (nq > 16) { nq /= 2; ks *= 2; }
+    const int by_regs = std::max(DEC_WEIGHT_VECS / nq, 1), by_red = 64 / std::max(maxm, 1);
+    return (long long)(waves / ks) * std::min(by_regs, by_red);
+  };
+  const long long up = groups_up * (F / rows_per_wg(H, UP_WAVES));
+  const long long down = groups_down * (H / rows_per_wg(F, DOWN_WAVES));
+  return std::max(up, down);
 }
 
 bool route_in_decode_supported(int T, int k, int E, int E_loc) {

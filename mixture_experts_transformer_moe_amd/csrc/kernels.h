@@ -46,6 +46,8 @@ hipError_t launch_grouped_gemm(int dtype, int epi, bool bias_f32, int BM, int BN
 
 // decode_ffn.hip
 bool decode_supported(int dtype, int H, int F);
+// work-groups of the larger decode expert launch (segment groups of each)
+long long decode_max_workgroups(int dtype, int H, int F, int maxm, long long groups_up, long long groups_down);
 // rp (nullable): route the batch inside the kernel from the gate logits (see RouteParams).
 bool route_in_decode_supported(int T, int k, int E, int E_loc);
 hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s,

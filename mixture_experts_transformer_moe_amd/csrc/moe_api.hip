@@ -204,6 +204,18 @@ moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl) {
   const int64_t seg_rows = std::min<int64_t>(p.C, kT);
   p.exp_maxm = pow2_at_least(std::max<int64_t>(seg_rows, 1));
   p.exp_decode = seg_rows <= 8 && decode_supported(p.dtype, p.H, p.F);
+  if (p.exp_decode) {
+    // the streaming kernels give every segment group (every assignment when
+    // they route the batch themselves) a work-group per block of weight rows,
+    // and each routed work-group first routes the whole batch: past about 8192
+    // work-groups per launch the grouped GEMM, whose tile list holds only the
+    // active experts' tiles, is faster (decode at 8 tokens: 350M 30 vs 54 us,
+    // 6.7B top-1 339 vs 371 us with <= 8192; 6.7B and 24B one-GPU shares with
+    // top-2 472 vs 304 and 1857 vs 1123 us with 16 k and 64 k work-groups)
+    const int64_t segs = std::min<int64_t>(p.E_loc, p.R_max);
+    const int64_t up_groups = route_in_decode_supported((int)p.T, p.k, p.E, p.E_loc) ? kT : segs;
+    if (decode_max_workgroups(p.dtype, p.H, p.F, p.exp_maxm, up_groups, segs) > 8192) p.exp_decode = false;
+  }
   // top-1 standard layers: the second expert kernel writes y itself (the decode
   // kernel or the second grouped GEMM's epilogue)
   p.fold_combine = p.k == 1 && !p.residual && p.R_max > 0;

@@ -84,6 +84,10 @@ WORKLOADS = {
     # 24B+MoE-128: one GPU's share of 16 experts (0..15), top-2, Zipf(1.0)
     "share_24b_moe128": LayerShape("share_24b_moe128", T=16384, H=8192, F=32768, E=128,
                                    E_loc=16, k=2, cf=1.25, dtype="f16", zipf_s=1.0),
+    # the same share at a decode step (8 tokens): expert rows of 16 / 64 KB, the
+    # second product's K split over four waves in the decode kernels
+    "decode_24b_share": LayerShape("decode_24b_share", T=8, H=8192, F=32768, E=128,
+                                   E_loc=16, k=2, cf=1.0, dtype="f16", zipf_s=1.0),
 }
 
 # Reduced versions of the large workloads: same structure (k, cf, skew, mode,

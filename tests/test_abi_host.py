@@ -56,7 +56,7 @@ def test_capacity_table_and_oracle_agree():
 
 def test_max_rows_of_benchmark_layers():
     expect = {"tiny": 256, "decode_350m_moe128": 8, "prefill_1p3b_moe128": 4096, "prmoe_residual": 2048,
-              "share_24b_moe128": 5120}
+              "share_24b_moe128": 5120, "decode_24b_share": 16}
     for name, shape in W.WORKLOADS.items():
         d = B.desc_from_shape(shape)
         C = oracle.capacity(shape.T, shape.E, shape.k, shape.cf)

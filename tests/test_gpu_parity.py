@@ -80,6 +80,16 @@ CASES = {
     # one local expert of 64: four tiles in the first GEMM, whose work-groups zero
     # ~1000 dropped / non-local tokens' rows each
     "gemm_fold_few_tiles": W.LayerShape("gfft", T=4096, H=256, F=512, E=64, E_loc=1, k=1, cf=1.0, dtype="f16"),
+    # decode kernels with K split over 2 / 4 waves (K = 16384 / 32768): the second
+    # product (long F), the first (long H), top-2 in bf16, and a residual layer
+    # whose dense MLP runs on the decode kernels
+    "decode_ksplit2_f": W.LayerShape("dk2f", T=8, H=512, F=16384, E=16, E_loc=16, k=1, cf=1.0, dtype="f16"),
+    "decode_ksplit4_f_k2_bf16": W.LayerShape("dk4f", T=4, H=1024, F=32768, E=4, E_loc=4, k=2, cf=2.0,
+                                             dtype="bf16"),
+    "decode_ksplit2_h": W.LayerShape("dk2h", T=8, H=16384, F=512, E=16, E_loc=16, k=1, cf=1.0, dtype="f16"),
+    "decode_ksplit4_h": W.LayerShape("dk4h", T=2, H=32768, F=1024, E=4, E_loc=4, k=1, cf=2.0, dtype="f16"),
+    "residual_decode_ksplit": W.LayerShape("rdk", T=4, H=512, F=16384, E=8, E_loc=8, k=1, cf=1.0, dtype="f16",
+                                           mlp_type="residual"),
     "e512_decode": W.LayerShape("e512d", T=8, H=512, F=512, E=512, E_loc=512, k=2, cf=1.0, dtype="f16"),
     "e512_gemm": W.LayerShape("e512g", T=600, H=256, F=512, E=512, E_loc=512, k=1, cf=4.0, dtype="f16"),
     "ragged_t13": W.LayerShape("t13", T=13, H=512, F=1024, E=16, E_loc=16, k=2, cf=1.0, dtype="f16"),
