@@ -24,9 +24,9 @@
 // reads and the MFMAs of a step ran one after the other; there the two halves
 // of the work-group run half a step apart, and the K steps reach three LDS
 // buffers (same swizzled layout) by direct-to-LDS buffer loads.
-// grouped_gemm_pp320_kernel: the same schedule on 320 x 256 tiles (one per
-// segment of 257..320 rows) with 80 x 128 wave blocks, two LDS stages and
-// sub-steps of 32 K.
+// grouped_gemm_pp2_kernel: the same schedule on 256 x 256 and 320 x 256 tiles
+// (one per segment of 129..320 rows) with 64 / 80 x 128 wave blocks, two LDS
+// stages and sub-steps of 32 K.
 //
 // Epilogues: bias + exact GeLU rounded to the I/O dtype (first expert GEMM), or
 // bias in fp32 (second GEMM and gate logits); the ping-pong tiles stage their
@@ -718,30 +718,33 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
   }
 }
 
-// Eight-wave 320 x 256 tiles for segments of 257..320 rows (the expert GEMMs of
-// a capacity-320 share): one work-group covers a whole segment, so each weight
-// tile is read once, and each wave holds an 80 x 128 block (160 accumulator
-// VGPRs), which reads 28 % fewer LDS fragment bytes per multiply than the
-// 80 x 64 blocks of the 160 x 256 tiles. Two LDS stages of 73.7 KB (256 weight
-// rows and 320 activation rows of 128 bytes of K, same swizzle) in two separate
+// Eight-wave BM x 256 tiles, BM = 256 or 320, for segments of 129..320 rows
+// (the expert GEMMs of a capacity-256 or -320 share): one work-group covers a
+// whole segment, so each weight tile is read once, and each wave holds a
+// BM / 4 x 128 block (at BM = 320: 160 accumulator VGPRs), which at BM = 320
+// reads 28 % fewer LDS fragment bytes per multiply than the 80 x 64 blocks of
+// 160 x 256 tiles. Two LDS stages (256 weight rows and BM activation rows of
+// 128 bytes of K, same swizzle; 73.7 KB at BM = 320) in two separate
 // arrays, so that the compiler sees which stage a direct-to-LDS load writes and
 // which one a fragment read reads, and adds no wait of its own between them.
-// Waves 0-3 (rows 0-159) and 4-7 (rows 160-319) run half a phase apart on
+// Waves 0-3 (rows 0 .. BM / 2 - 1) and 4-7 (the rest) run half a phase apart on
 // sub-steps of 32 K (one sub-step's fragments, 52 VGPRs, fit beside the
 // accumulators): on every SIMD one wave multiplies while the other reads its
-// fragments. Each group loads its half of a stage (its 160 activation rows and
-// 128 of the weight rows) in its memory phase of sub-step 2 s, after the
+// fragments. Each group loads its half of a stage (its BM / 2 activation rows
+// and 128 of the weight rows) in its memory phase of sub-step 2 s, after the
 // barrier that frees the buffer, and waits for its loads (vmcnt 0) right before
 // the barrier after which stage s + 1 is first read: group 0 at the end of its
 // multiply phase of sub-step 2 s + 1, group 1 at the end of its memory phase
 // of that sub-step (3.5 and 2.5 phases after the issue). No load is then in
 // flight at the loop's back edge, where the compiler waits for all of them.
-template <typename DT, int EPI, typename BiasT, bool WNT>
-__global__ __launch_bounds__(512, 2) void grouped_gemm_pp320_kernel(GemmParams p) {
+template <typename DT, int BM, int EPI, typename BiasT, bool WNT>
+__global__ __launch_bounds__(512, 2) void grouped_gemm_pp2_kernel(GemmParams p) {
   using T = typename DT::T;
-  constexpr int BM = 320, BN = 256;
-  constexpr int TN = 8, TM = 5;
-  constexpr int NCH = 9;                       // 8-row chunks per wave per stage: (16 + 20) per group / 4
+  static_assert(BM == 256 || BM == 320, "256- or 320-row tiles");
+  constexpr int BN = 256;
+  constexpr int HB = BM / 2, WB = BM / 4;      // rows of a group, of a wave's block
+  constexpr int TN = 8, TM = WB / 16;
+  constexpr int NCH = (16 + HB / 8) / 4;       // 8-row chunks per wave per stage: 16 weight + HB / 8 activation per group
   constexpr int STAGE = (BN + BM) * LDS_ROW;
   __shared__ __attribute__((aligned(16))) char lds0[STAGE];
   __shared__ __attribute__((aligned(16))) char lds1[STAGE];
@@ -753,11 +756,11 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp320_kernel(GemmParams p
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = wave >> 2;          // row half: activation rows 160 g ..
-  const int wm = (wave >> 1) & 1;   // 80-row block within the half
+  const int g = wave >> 2;          // row half: activation rows HB g ..
+  const int wm = (wave >> 1) & 1;   // WB-row block within the half
   const int wn = wave & 1;          // 128-column block
   const int wl = wave & 3;          // wave within its group (load chunks)
-  const int mw = m0 + g * 160 + wm * 80;   // first row of this wave's block
+  const int mw = m0 + g * HB + wm * WB;   // first row of this wave's block
   const bool fold = EPI == EPI_F32 && p.fold_y && !extra;
   int ftok[TM];
   float fw[TM];
@@ -769,7 +772,7 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp320_kernel(GemmParams p
                              : reinterpret_cast<const char*>(p.B) + (long long)seg * p.b_stride * (long long)sizeof(T);
   const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(bbase + (long long)nt * BN * p.K * (long long)sizeof(T));
   // chunk i of this wave: c = wl + 4 i; c < 16: weight rows 128 g + 8 c; else
-  // activation rows 160 g + 8 (c - 16) (clamped into the segment). Lane l lands
+  // activation rows HB g + 8 (c - 16) (clamped into the segment). Lane l lands
   // in row l / 8 of the chunk, 16-byte slot l % 8, so it loads column
   // (l % 8) ^ (l / 8) (the XOR swizzle).
   const int col = ((lane & 7) ^ (lane >> 3)) * 16;
@@ -783,11 +786,11 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp320_kernel(GemmParams p
       voff[i] = (unsigned)(row * p.K * (int)sizeof(T)) + col;
       ldst[i] = (g * 128 + c * 8) * LDS_ROW;
     } else {
-      int r = m0 + g * 160 + (c - 16) * 8 + (lane >> 3);
+      int r = m0 + g * HB + (c - 16) * 8 + (lane >> 3);
       if (r >= r1) r = r1 - 1;
       const long long arow = (p.a_rows && !extra) ? (long long)p.a_rows[r] : (long long)r;
       voff[i] = (unsigned)(arow * p.K * (long long)sizeof(T)) + col;
-      ldst[i] = BN * LDS_ROW + (g * 160 + (c - 16) * 8) * LDS_ROW;
+      ldst[i] = BN * LDS_ROW + (g * HB + (c - 16) * 8) * LDS_ROW;
     }
   }
 
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp320_kernel(GemmParams p
     _Pragma("unroll") for (int i = 0; i < TN; ++i)                                       \
       fa[i] = *reinterpret_cast<const uint4*>((BUF) + (wn * 128 + i * 16 + frag_row) * LDS_ROW + fc_); \
     _Pragma("unroll") for (int j = 0; j < TM; ++j)                                       \
-      fb[j] = *reinterpret_cast<const uint4*>((BUF) + (BN + g * 160 + wm * 80 + j * 16 + frag_row) * LDS_ROW + fc_); \
+      fb[j] = *reinterpret_cast<const uint4*>((BUF) + (BN + g * HB + wm * WB + j * 16 + frag_row) * LDS_ROW + fc_); \
   }
 #define P3_MATH                                                                          \
   {                                                                                      \
@@ -930,11 +933,11 @@ static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) 
     // (launch_grouped_gemm refuses float-bias 256-column tiles and operands
     // beyond 32-bit offsets before getting here)
     if constexpr (!std::is_same<BiasT, float>::value) {
-      if constexpr (BM == 320) {
+      if constexpr (BM == 256 || BM == 320) {
         if (p.stream_w)
-          MOE_LAUNCH((grouped_gemm_pp320_kernel<DT, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+          MOE_LAUNCH((grouped_gemm_pp2_kernel<DT, BM, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
         else
-          MOE_LAUNCH((grouped_gemm_pp320_kernel<DT, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
+          MOE_LAUNCH((grouped_gemm_pp2_kernel<DT, BM, EPI, BiasT, false>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
       } else {
         if (p.stream_w)
           MOE_LAUNCH((grouped_gemm_pp_kernel<DT, BM, EPI, BiasT, true>), g, dim3(NTH), 0, s, ev.start, ev.stop, p);
@@ -975,11 +978,12 @@ static bool launch_bm(int BM, int epi, bool bias_f32, const GemmParams& p, int g
   return false;
 }
 
-// 128 x 256, 160 x 256 and 320 x 256 tiles, eight waves: segments of 65..320 rows and the dense MLP
+// 128 x 256, 256 x 256 and 320 x 256 tiles, eight waves: segments of 65..320 rows and the dense MLP
 template <typename DT>
 static bool launch_big(int BM, int epi, bool bias_f32, const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   switch (BM) {
     case 128: launch_epi<DT, 128, 256>(epi, bias_f32, p, grid, s, ev); return true;
+    case 256: launch_epi<DT, 256, 256>(epi, bias_f32, p, grid, s, ev); return true;
     case 320: launch_epi<DT, 320, 256>(epi, bias_f32, p, grid, s, ev); return true;
   }
   return false;

@@ -257,8 +257,9 @@ moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl) {
   p.BN1 = (p.F % 128 == 0) ? 128 : 64;
   p.BN2 = (p.H % 128 == 0) ? 128 : 64;
   // segments of more than 64 rows: eight-wave 128 x 256 or 160 x 256 tiles
-  // (320 when one tile covers a segment that would need three 128-row tiles:
-  // each weight tile is then read once, by a work-group of 80 x 128 wave blocks)
+  // (256 / 320 when one tile covers a segment that would need two / three
+  // 128-row tiles: each weight tile is then read once, by a work-group of
+  // 64 / 80 x 128 wave blocks)
   // (they address their operands with 32-bit byte offsets: activations x,
   // x_disp and h, at most max(T, R_max) rows of max(H, F), and one expert's or
   // the MLP's weights, H x F, must each stay below 4 GB)
@@ -267,6 +268,7 @@ moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl) {
   const bool big_ok = p.dtype != MOE_DTYPE_F32 && p.F % 256 == 0 && p.H % 256 == 0 && p.off32;
   if (p.BM == 128 && big_ok) {
     p.BN1 = p.BN2 = 256;
+    if (seg_rows > 128 && seg_rows <= 256) p.BM = 256;
     if (seg_rows > 256 && seg_rows <= 320) p.BM = 320;
   }
   {

@@ -1,6 +1,6 @@
 """Address bounds of the ping-pong grouped GEMM's direct-to-LDS loads (CPU only).
 
-The eight-wave 128 x 256 / 320 x 256 tiles load each K step through two buffer
+The eight-wave 128 / 256 / 320 x 256 tiles load each K step through two buffer
 descriptors without range checks: the weight descriptor starts at the tile's
 first weight row, the activation descriptor at row 0 of the activation matrix.
 This replays the kernel's per-lane offset formulas for every wave, lane and
@@ -39,37 +39,42 @@ def pp_offsets(BM, K, esz, m0, r1, a_rows=None):
     return out
 
 
-def pp320_offsets(K, esz, m0, r1, a_rows=None):
-    """The same for the 320 x 256 tiles: each group (waves 0-3, 4-7) loads 128
-    weight rows and its 160 activation rows per stage, nine 8-row chunks per
-    wave (chunk c = wave % 4 + 4 i: c < 16 weight rows 128 g + 8 c, else
-    activation rows 160 g + 8 (c - 16), clamped into the segment)."""
+def pp2_offsets(BM, K, esz, m0, r1, a_rows=None):
+    """The same for the 256 x 256 / 320 x 256 tiles: each group (waves 0-3, 4-7)
+    loads 128 weight rows and its BM / 2 activation rows per stage, (16 + BM /
+    16) / 4 8-row chunks per wave (chunk c = wave % 4 + 4 i: c < 16 weight rows
+    128 g + 8 c, else activation rows BM / 2 g + 8 (c - 16), clamped into the
+    segment)."""
+    HB = BM // 2
+    NCH = (16 + HB // 8) // 4
     out = []
     for wave in range(8):
         g, wl = wave // 4, wave % 4
         for lane in range(64):
             col = ((lane & 7) ^ (lane >> 3)) * 16
-            for i in range(9):
+            for i in range(NCH):
                 c = wl + 4 * i
                 if i < 4:
                     row = g * 128 + c * 8 + (lane >> 3)
                     out.append(("w", row * K * esz + col))
                 else:
-                    r = min(m0 + g * 160 + (c - 16) * 8 + (lane >> 3), r1 - 1)
+                    r = min(m0 + g * HB + (c - 16) * 8 + (lane >> 3), r1 - 1)
                     arow = a_rows[r] if a_rows is not None else r
                     out.append(("a", arow * K * esz + col))
     return out
 
 
-def pp320_lds_rows():
-    """LDS rows each wave's chunks land in (weights 0-255, activations 256-575):
+def pp2_lds_rows(BM):
+    """LDS rows each wave's chunks land in (weights 0-255, activations 256 ..):
     every row of a stage exactly once."""
+    HB = BM // 2
+    NCH = (16 + HB // 8) // 4
     rows = []
     for wave in range(8):
         g, wl = wave // 4, wave % 4
-        for i in range(9):
+        for i in range(NCH):
             c = wl + 4 * i
-            base = g * 128 + c * 8 if i < 4 else 256 + g * 160 + (c - 16) * 8
+            base = g * 128 + c * 8 if i < 4 else 256 + g * HB + (c - 16) * 8
             rows.extend(range(base, base + 8))
     return rows
 
@@ -77,7 +82,7 @@ def pp320_lds_rows():
 def check_tile(BM, K, esz, m0, r1, a_total_rows, a_rows=None):
     nk = K * esz // 128
     last = (nk - 1) * 128 + 16          # the last step's 16 bytes past the base offset
-    offs = pp320_offsets(K, esz, m0, r1, a_rows) if BM == 320 else pp_offsets(BM, K, esz, m0, r1, a_rows)
+    offs = pp2_offsets(BM, K, esz, m0, r1, a_rows) if BM in (256, 320) else pp_offsets(BM, K, esz, m0, r1, a_rows)
     for kind, off in offs:
         assert off >= 0
         if kind == "w":
@@ -86,7 +91,7 @@ def check_tile(BM, K, esz, m0, r1, a_total_rows, a_rows=None):
             assert off + last <= a_total_rows * K * esz, (BM, kind, off, a_total_rows)
 
 
-@pytest.mark.parametrize("BM", [128, 320])
+@pytest.mark.parametrize("BM", [128, 256, 320])
 def test_expert_tiles_stay_inside_operands(BM):
     # first GEMM: A = x [T, H] read through slot_token; second GEMM: A = h [R_max, F]
     for T, H, seg in [(150, 256, 150), (1024, 512, 300), (20, 512, 17), (129, 256, 129)]:
@@ -98,16 +103,17 @@ def test_expert_tiles_stay_inside_operands(BM):
                 check_tile(BM, H, 2, r0 + mt * BM, r1, r1)       # h rows
 
 
-@pytest.mark.parametrize("BM", [128, 320])
+@pytest.mark.parametrize("BM", [128, 256, 320])
 def test_dense_mlp_tiles_stay_inside_x(BM):
     for T in (1, 100, 150, 160, 300):
         for mt in range((T + BM - 1) // BM):
             check_tile(BM, 512, 2, mt * BM, T, T)
 
 
-def test_pp320_stage_rows_each_loaded_once():
-    rows = pp320_lds_rows()
-    assert sorted(rows) == list(range(576))
+@pytest.mark.parametrize("BM", [256, 320])
+def test_pp2_stage_rows_each_loaded_once(BM):
+    rows = pp2_lds_rows(BM)
+    assert sorted(rows) == list(range(256 + BM))
 
 
 def test_plan_picks_320_rows_for_short_batches():

@@ -52,11 +52,13 @@ CASES = {
     # weights streamed, the MLP's cached (two copies of the K loop)
     "residual_bm320": W.LayerShape("r160", T=1024, H=512, F=1024, E=4, E_loc=4, k=1, cf=1.25, dtype="f16",
                                    mlp_type="residual"),
-    # 128 x 256 ping-pong tiles: with the dense MLP's tiles in the same launches,
-    # and in bf16 with top-2 (segments of up to C = 150 rows)
+    # 128 x 256 ping-pong tiles with the dense MLP's tiles in the same launches;
+    # 256 x 256 tiles in bf16 with top-2 (segments of up to C = 150 rows); the
+    # folded combine on 128 x 256 tiles (C = 128)
     "residual_bm128": W.LayerShape("r128", T=1024, H=512, F=1024, E=8, E_loc=8, k=1, cf=1.0, dtype="f16",
                                    mlp_type="residual"),
-    "gemm_bm128_bf16_k2": W.LayerShape("g128b", T=600, H=256, F=512, E=8, E_loc=8, k=2, cf=1.0, dtype="bf16"),
+    "gemm_bm256_bf16_k2": W.LayerShape("g128b", T=600, H=256, F=512, E=8, E_loc=8, k=2, cf=1.0, dtype="bf16"),
+    "gemm_bm128_fold": W.LayerShape("g128f", T=1024, H=256, F=512, E=8, E_loc=8, k=1, cf=1.0, dtype="f16"),
     # 320 x 256 tiles over a batch of fewer than 320 tokens (C = 300, segments of
     # 150 rows): every activation load of the first GEMM must stay inside x's
     # 150 rows
