@@ -728,8 +728,8 @@ __global__ __launch_bounds__(512, 2) void grouped_gemm_pp_kernel(GemmParams p) {
 // arrays, so that the compiler sees which stage a direct-to-LDS load writes and
 // which one a fragment read reads, and adds no wait of its own between them.
 // Waves 0-3 (rows 0 .. BM / 2 - 1) and 4-7 (the rest) run half a phase apart on
-// sub-steps of 32 K (one sub-step's fragments, 52 VGPRs, fit beside the
-// accumulators): on every SIMD one wave multiplies while the other reads its
+// sub-steps of 32 K (one sub-step's fragments, 48 / 52 VGPRs at BM = 256 / 320,
+// fit beside the accumulators): on every SIMD one wave multiplies while the other reads its
 // fragments. Each group loads its half of a stage (its BM / 2 activation rows
 // and 128 of the weight rows) in its memory phase of sub-step 2 s, after the
 // barrier that frees the buffer, and waits for its loads (vmcnt 0) right before
