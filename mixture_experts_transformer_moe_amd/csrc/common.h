@@ -233,6 +233,15 @@ struct DecodeParams {
   void* out;              // down: fp32 [rows][H], or the layer output [T][H] when the combine is folded in
   const int* slot_token;  // folded combine: token of each row
   const float* topk_w;    // folded combine: top-1 weight of each token
+  // optional dense segment, the residual MLP over rows [0, dM) of x (dM <= 8),
+  // served by work-groups after those of the ngroups expert segment groups:
+  // weights dw1 [F][H], db1 [F], dw2 [H][F], db2 [H]; hidden dh [dM][F] (I/O
+  // dtype); output dout fp32 [dM][H]. dM = 0: none
+  int dM;
+  int ngroups;            // expert segment groups of the launch (set by the launcher)
+  const void* dw1; const void* db1; const void* dw2; const void* db2;
+  void* dh;
+  float* dout;
 };
 
 // Routing of a decode-sized batch done inside the first expert kernel: every

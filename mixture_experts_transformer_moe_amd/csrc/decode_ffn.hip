@@ -315,7 +315,65 @@ __device__ inline float ksplit_sum(float s, int wave, int lane, bool& keep) {
   return s;
 }
 
-template <typename DT, int MAXM, int NQ, int KS>
+// The dense segment's work-groups (the residual MLP over the dM <= 8 rows of
+// x, all of them at once: 8 activation rows per weight row, rows past dM
+// repeat row 0 and are not stored). Chunk c covers the weight rows of one
+// work-group, as for an expert segment.
+#define DENSE_MAXM 8
+template <typename DT, int NQ, int KS>
+__device__ inline void dense_up_wg(const DecodeParams& p, int chunk) {
+  using T = typename DT::T;
+  constexpr int RPW = DecRows<NQ, DENSE_MAXM>::RPW;
+  constexpr int SH = 6 - ilog2(RPW * DENSE_MAXM);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long H = p.H, F = p.F;
+  const int f0 = chunk * (UP_WAVES / KS) * RPW + (wave / KS) * RPW;
+  const long long kofs = (long long)(wave % KS) * (H / KS);
+  const int v = lane >> SH;
+  const int oi = v / DENSE_MAXM, om = v - (v / DENSE_MAXM) * DENSE_MAXM;
+  uint4 wv[RPW][NQ];
+  load_rows<DT, NQ, RPW>(wv, reinterpret_cast<const T*>(p.dw1) + (long long)f0 * H + kofs, H);
+  const T bias_raw = gload(reinterpret_cast<const T*>(p.db1) + f0 + oi);
+  __builtin_amdgcn_sched_barrier(0);
+  const int M = min(p.dM, DENSE_MAXM);
+  const T* x = reinterpret_cast<const T*>(p.x);
+  const T* act[DENSE_MAXM];
+#pragma unroll
+  for (int m = 0; m < DENSE_MAXM; ++m) act[m] = x + (long long)(m < M ? m : 0) * H + kofs;
+  bool keep;
+  const float s = ksplit_sum<KS, UP_WAVES>(dot_rows<DT, DENSE_MAXM, NQ, RPW>(wv, act), wave, lane, keep);
+  if (keep && (lane & ((1 << SH) - 1)) == 0 && om < M)
+    reinterpret_cast<T*>(p.dh)[(long long)om * F + f0 + oi] =
+        DT::from_f(pin_f32(gelu_erf(s + DT::to_f(bias_raw))));
+}
+
+template <typename DT, int NQ, int KS>
+__device__ inline void dense_down_wg(const DecodeParams& p, int chunk) {
+  using T = typename DT::T;
+  constexpr int RPW = DecRows<NQ, DENSE_MAXM>::RPW;
+  constexpr int SH = 6 - ilog2(RPW * DENSE_MAXM);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long H = p.H, F = p.F;
+  const int j0 = chunk * (DOWN_WAVES / KS) * RPW + (wave / KS) * RPW;
+  const long long kofs = (long long)(wave % KS) * (F / KS);
+  const int v = lane >> SH;
+  const int oi = v / DENSE_MAXM, om = v - (v / DENSE_MAXM) * DENSE_MAXM;
+  uint4 wv[RPW][NQ];
+  load_rows<DT, NQ, RPW>(wv, reinterpret_cast<const T*>(p.dw2) + (long long)j0 * F + kofs, F);
+  const T bias_raw = gload(reinterpret_cast<const T*>(p.db2) + j0 + oi);
+  __builtin_amdgcn_sched_barrier(0);
+  const int M = min(p.dM, DENSE_MAXM);
+  const T* h = reinterpret_cast<const T*>(p.dh);
+  const T* act[DENSE_MAXM];
+#pragma unroll
+  for (int m = 0; m < DENSE_MAXM; ++m) act[m] = h + (long long)(m < M ? m : 0) * F + kofs;
+  bool keep;
+  const float s = ksplit_sum<KS, DOWN_WAVES>(dot_rows<DT, DENSE_MAXM, NQ, RPW>(wv, act), wave, lane, keep);
+  if (keep && (lane & ((1 << SH) - 1)) == 0 && om < M)
+    p.dout[(long long)om * H + j0 + oi] = s + DT::to_f(bias_raw);
+}
+
+template <typename DT, int MAXM, int NQ, int KS, bool DENSE>
 __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(RouteParams rp, DecodeParams p) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
@@ -324,6 +382,13 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(RouteParams rp
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nchunk = p.F / ((UP_WAVES / KS) * RPW);
+  if constexpr (DENSE) {   // the dense segment's work-groups follow the expert groups'
+    const int nexp = p.ngroups * nchunk;
+    if ((int)blockIdx.x >= nexp) {
+      dense_up_wg<DT, NQ, KS>(p, (int)blockIdx.x - nexp);
+      return;
+    }
+  }
   const int g = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - g * nchunk;
   const long long H = p.H, F = p.F;
@@ -385,7 +450,7 @@ __global__ __launch_bounds__(UP_WAVES * 64) void decode_up_kernel(RouteParams rp
   }
 }
 
-template <typename DT, int MAXM, int NQ, bool FUSE, int KS>
+template <typename DT, int MAXM, int NQ, bool FUSE, int KS, bool DENSE>
 __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodeParams p) {
   using T = typename DT::T;
   constexpr int RPW = DecRows<NQ, MAXM>::RPW;
@@ -394,6 +459,13 @@ __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DecodePara
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nchunk = p.H / ((DOWN_WAVES / KS) * RPW);
+  if constexpr (DENSE) {   // the dense segment's work-groups follow the expert groups'
+    const int nexp = p.ngroups * nchunk;
+    if ((int)blockIdx.x >= nexp) {
+      dense_down_wg<DT, NQ, KS>(p, (int)blockIdx.x - nexp);
+      return;
+    }
+  }
   const int g = blockIdx.x / nchunk;
   const int chunk = blockIdx.x - g * nchunk;
   int seg = 0, r0 = 0, r1 = p.M;
@@ -692,27 +764,44 @@ struct LaunchEv {
   hipEvent_t start, stop;
 };
 
+// (p.dM > 0: the dense segment's work-groups are appended to the grid)
 template <typename DT, int MAXM, int NQ, int KS>
 static hipError_t launch_up_t(const DecodeParams& p, const RouteParams& rp, int grid_segs, hipStream_t s,
                               LaunchEv ev) {
-  constexpr int RPW = DecRows<NQ, MAXM>::RPW;
+  constexpr int RPW = DecRows<NQ, MAXM>::RPW, RPWD = DecRows<NQ, DENSE_MAXM>::RPW;
   const int grid = grid_segs * (p.F / ((UP_WAVES / KS) * RPW));
   const size_t lds = rp.z ? sizeof(int) * route_lds_ints(rp.T, rp.k, rp.R_max) : 0;
-  MOE_LAUNCH((decode_up_kernel<DT, MAXM, NQ, KS>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start, ev.stop, rp,
-             p);
+  if (p.dM > 0) {
+    DecodeParams q = p;
+    q.ngroups = grid_segs;
+    const int gd = grid + p.F / ((UP_WAVES / KS) * RPWD);
+    MOE_LAUNCH((decode_up_kernel<DT, MAXM, NQ, KS, true>), dim3(gd), dim3(UP_WAVES * 64), lds, s, ev.start, ev.stop,
+               rp, q);
+  } else {
+    MOE_LAUNCH((decode_up_kernel<DT, MAXM, NQ, KS, false>), dim3(grid), dim3(UP_WAVES * 64), lds, s, ev.start,
+               ev.stop, rp, p);
+  }
   return hipGetLastError();
 }
 
 template <typename DT, int MAXM, int NQ, int KS>
 static hipError_t launch_down_t(const DecodeParams& p, int grid_segs, bool fuse, hipStream_t s, LaunchEv ev) {
-  constexpr int RPW = DecRows<NQ, MAXM>::RPW;
+  constexpr int RPW = DecRows<NQ, MAXM>::RPW, RPWD = DecRows<NQ, DENSE_MAXM>::RPW;
   const int grid = grid_segs * (p.H / ((DOWN_WAVES / KS) * RPW));
-  if (fuse)
-    MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, true, KS>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s, ev.start,
-               ev.stop, p);
-  else
-    MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, false, KS>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s, ev.start,
-               ev.stop, p);
+  if (p.dM > 0) {   // (the dense output is added by the combine kernel: no folded combine here)
+    if (fuse) return hipErrorInvalidValue;
+    DecodeParams q = p;
+    q.ngroups = grid_segs;
+    const int gd = grid + p.H / ((DOWN_WAVES / KS) * RPWD);
+    MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, false, KS, true>), dim3(gd), dim3(DOWN_WAVES * 64), 0, s,
+               ev.start, ev.stop, q);
+  } else if (fuse) {
+    MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, true, KS, false>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s,
+               ev.start, ev.stop, p);
+  } else {
+    MOE_LAUNCH((decode_down_kernel<DT, MAXM, NQ, false, KS, false>), dim3(grid), dim3(DOWN_WAVES * 64), 0, s,
+               ev.start, ev.stop, p);
+  }
   return hipGetLastError();
 }
 
@@ -837,7 +926,9 @@ bool route_in_decode_supported(int T, int k, int E, int E_loc) {
 
 hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid_segs, hipStream_t s,
                             hipEvent_t ev0, hipEvent_t ev1, const RouteParams* rp) {
-  if (grid_segs <= 0) return hipSuccess;
+  if (p.dM > DENSE_MAXM || p.dM < 0) return hipErrorInvalidValue;
+  if (grid_segs <= 0 && p.dM == 0) return hipSuccess;
+  if (grid_segs < 0) grid_segs = 0;
   const LaunchEv ev{ev0, ev1};
   const RouteParams none{};
   const RouteParams& r = rp ? *rp : none;
@@ -847,7 +938,9 @@ hipError_t launch_decode_up(int dtype, int maxm, const DecodeParams& p, int grid
 
 hipError_t launch_decode_down(int dtype, int maxm, const DecodeParams& p, int grid_segs, bool fuse_combine,
                               hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  if (grid_segs <= 0) return hipSuccess;
+  if (p.dM > DENSE_MAXM || p.dM < 0) return hipErrorInvalidValue;
+  if (grid_segs <= 0 && p.dM == 0) return hipSuccess;
+  if (grid_segs < 0) grid_segs = 0;
   // the folded combine reads the row -> token map and the gate weights
   if (fuse_combine && (!p.slot_token || !p.topk_w || !p.out)) return hipErrorInvalidValue;
   const LaunchEv ev{ev0, ev1};

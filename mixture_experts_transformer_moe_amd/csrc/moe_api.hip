@@ -118,8 +118,9 @@ struct Plan {
   // dense MLP
   bool dense_decode;
   bool dense_in_experts;  // residual MLP as an extra segment of the expert GEMM launches
+  bool dense_in_decode;   // residual MLP as extra work-groups of the two decode expert launches
   int mt_extra;           // its row tiles
-  int dense_maxm, dBM, dBN1, dBN2;
+  int dBM, dBN1, dBN2;
   // workspace offsets (bytes)
   size_t o_z, o_idx, o_w, o_rank, o_blk, o_demand, o_off, o_slot_token, o_token_slot;
   size_t o_h, o_ydisp, o_list1, o_list2, o_count;
@@ -278,13 +279,15 @@ moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl) {
     p.mt_bound = (int)mtb;
     if (p.F / p.BN1 >= 65536 || p.H / p.BN2 >= 65536) return fail(MOE_ERR_UNSUPPORTED, "too many column tiles");
   }
-  p.dense_maxm = pow2_at_least(std::max<int64_t>(p.T, 1));
   p.dense_decode = p.T <= 8 && decode_supported(p.dtype, p.H, p.F);
   // GEMM path with 64-row expert tiles: the dense MLP's tiles join the expert
   // GEMM launches (its L2-resident weights overlap the experts' weight
   // streaming). With smaller expert tiles the MLP would run on tiles too thin
   // for its T rows (measured slower), so it keeps its own launches.
   p.dense_in_experts = p.residual && !p.exp_decode && !p.dense_decode && p.BM >= 64;
+  // decode path: the dense MLP's work-groups join the two expert launches (not
+  // the one-launch kernel, set below)
+  p.dense_in_decode = p.residual && p.exp_decode && p.dense_decode && !p.fused_decode;
   // weight-streaming tiles (<= 64 rows) of a second GEMM with long weight rows:
   // 64-column tiles halve each work-group's share of the weights (F = 8192,
   // fp16: 1 MB instead of 2 MB), so the work-groups left over when the tile
@@ -507,6 +510,15 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
     d.out = y_fold ? y_fold : (void*)ydisp;
     d.slot_token = slot_token;
     d.topk_w = topk_w;
+    if (with_dense && p.dense_in_decode) {   // the residual MLP's work-groups in the same two launches
+      d.dM = (int)p.T;
+      d.dw1 = w->mlp_w1;
+      d.db1 = w->mlp_b1;
+      d.dw2 = w->mlp_w2;
+      d.db2 = w->mlp_b2;
+      d.dh = wsp<void>(ws, p.o_dh);
+      d.dout = wsp<float>(ws, p.o_dense);
+    }
     const int gsegs = (int)std::min<int64_t>(p.E_loc, p.R_max);
     // routed in the kernel: one group of work-groups per assignment (see route_phase1)
     const int gsegs_up = route ? (int)(p.T * p.k) : gsegs;
@@ -600,20 +612,21 @@ moe_status_t run_experts(const Plan& p, const void* x, const int* a_rows, const 
 moe_status_t run_dense(const Plan& p, const void* x, const moe_layer_weights_t* w, float* out, void* ws,
                        hipStream_t s) {
   if (p.dense_decode) {
+    // the decode kernels' dense work-groups alone (no expert groups): the same
+    // code and arithmetic as when they join the expert launches
     DecodeParams d{};
     d.x = x;
-    d.M = (int)p.T;
-    d.nseg = 1;
     d.H = p.H;
     d.F = p.F;
-    d.w1 = w->mlp_w1;
-    d.b1 = w->mlp_b1;
-    d.w2 = w->mlp_w2;
-    d.b2 = w->mlp_b2;
-    d.h = wsp<void>(ws, p.o_dh);
-    d.out = out;
-    HIP_TRY(launch_decode_up(p.dtype, p.dense_maxm, d, 1, s), "dense mlp up (decode)");
-    HIP_TRY(launch_decode_down(p.dtype, p.dense_maxm, d, 1, false, s), "dense mlp down (decode)");
+    d.dM = (int)p.T;
+    d.dw1 = w->mlp_w1;
+    d.db1 = w->mlp_b1;
+    d.dw2 = w->mlp_w2;
+    d.db2 = w->mlp_b2;
+    d.dh = wsp<void>(ws, p.o_dh);
+    d.dout = out;
+    HIP_TRY(launch_decode_up(p.dtype, 1, d, 0, s), "dense mlp up (decode)");
+    HIP_TRY(launch_decode_down(p.dtype, 1, d, 0, false, s), "dense mlp down (decode)");
     return MOE_OK;
   }
   void* h = wsp<void>(ws, p.o_dh);
@@ -699,7 +712,7 @@ moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out) {
   out->expert_path = p.exp_decode ? MOE_EXPERTS_STREAM : MOE_EXPERTS_GROUPED_GEMM;
   out->dispatch_in_expert_kernel = p.route_in_up ? 1 : 0;
   out->combine_in_expert_kernel = p.fold_combine ? 1 : 0;
-  out->dense_in_expert_kernels = p.dense_in_experts ? 1 : 0;
+  out->dense_in_expert_kernels = (p.dense_in_experts || p.dense_in_decode) ? 1 : 0;
   out->tile_rows = p.exp_decode ? 0 : p.BM;
   out->tile_cols_w1 = p.exp_decode ? 0 : p.BN1;
   out->tile_cols_w2 = p.exp_decode ? 0 : p.BN2;
@@ -708,7 +721,7 @@ moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out) {
   // MLP's two unless inside the expert GEMMs; combine
   out->experts_one_launch = p.fused_decode ? 1 : 0;
   out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) + (p.fused_decode ? 1 : 2) +
-                  ((p.residual && !p.dense_in_experts) ? 2 : 0) + (p.fold_combine ? 0 : 1);
+                  ((p.residual && !p.dense_in_experts && !p.dense_in_decode) ? 2 : 0) + (p.fold_combine ? 0 : 1);
   return MOE_OK;
 }
 
@@ -862,13 +875,13 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   ST_TRY(record(e.dispatch_end, stream));
   ST_TRY(record(e.ffn_begin, stream));
   float* ydisp = wsp<float>(ws, p.o_ydisp);
-  if (p.R_max > 0 || p.dense_in_experts)
+  if (p.R_max > 0 || p.dense_in_experts || p.dense_in_decode)
     ST_TRY(run_experts(p, x, slot_token, offsets, w, ydisp, ws, stream, y_fold, slot_token, tw, ev,
                        p.route_in_up ? &rp : nullptr, true, true));
   float* dense = nullptr;
   if (p.residual) {
     dense = wsp<float>(ws, p.o_dense);
-    if (!p.dense_in_experts) ST_TRY(run_dense(p, x, w, dense, ws, stream));
+    if (!p.dense_in_experts && !p.dense_in_decode) ST_TRY(run_dense(p, x, w, dense, ws, stream));
   }
   ST_TRY(record(e.ffn_end, stream));
   ST_TRY(record(e.combine_begin, stream));

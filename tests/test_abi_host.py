@@ -127,6 +127,9 @@ def test_layer_plan_paths():
         assert got == (gate, experts, disp, comb, launches), (name, pl)
         assert pl["dense_in_expert_kernels"] == (name == "prmoe_residual"), (name, pl)
         assert not pl["experts_one_launch"], (name, pl)
+    # residual decode: the dense MLP's work-groups join the two expert launches
+    rd = B.moe_layer_plan(B.desc_from_shape(W.REDUCED["residual_reduced"].with_(T=8, H=512, F=1024)))
+    assert (rd["expert_path"], rd["dense_in_expert_kernels"], rd["launches"]) == ("stream", True, 1 + 0 + 2 + 1), rd
     # the one-launch decode kernel only on request, and only on the routed decode path
     one = B.moe_layer_plan(B.desc_from_shape(W.WORKLOADS["decode_350m_moe128"].with_(one_launch=True)))
     assert one["experts_one_launch"] and one["launches"] == 2
