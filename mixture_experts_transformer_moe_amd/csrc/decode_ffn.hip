@@ -15,6 +15,9 @@
 // segment's activation rows and a single multi-value wave reduction sums the
 // RPW x MAXM dot products. Work-group g x c takes the g-th non-empty segment
 // (found by each wave on its own from the offsets) and the c-th block of rows.
+// Rows longer than 16 vectors per lane are split over 2 or 4 waves whose sums
+// meet in LDS. A residual layer's dense MLP (all of the batch's rows) can ride
+// in the same two launches as extra work-groups after the expert groups'.
 #include <algorithm>
 
 #include "common.h"
