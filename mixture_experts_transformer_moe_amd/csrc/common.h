@@ -84,16 +84,44 @@ __device__ inline float pin_f32(float v) {
 // Exact GeLU u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with the device erff.
 __device__ inline float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
 
-// Wave-wide sum (all lanes get the result).
+// Lane moves inside rows of 16 lanes through DPP (an operand modifier of the
+// VALU instruction, no LDS round trip as a bpermute shuffle takes): xor 1 and
+// xor 2 inside each quad, then the mirrors that pair lane i with lane 7 - i in
+// each half row and with 15 - i in each row. Once the two quad steps have given
+// every lane of a quad the same value, the mirrors pair quads and half rows as
+// xor 4 and xor 8 would, so four steps leave a row's result in all its lanes.
+// Every lane of the wave must be active.
+#define MOE_DPP_XOR1 0xB1      // quad_perm [1, 0, 3, 2]
+#define MOE_DPP_XOR2 0x4E      // quad_perm [2, 3, 0, 1]
+#define MOE_DPP_HMIRROR 0x141  // row_half_mirror
+#define MOE_DPP_MIRROR 0x140   // row_mirror
+template <int CTRL>
+__device__ inline int dpp_mov(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+  return __builtin_bit_cast(float, dpp_mov<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ inline float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Wave-wide sum (all lanes get the result): rows reduced by DPP, then the four
+// row sums added as (r0 + r1) + (r2 + r3).
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
-  return v;
+  v += dpp_mov<MOE_DPP_XOR1>(v);
+  v += dpp_mov<MOE_DPP_XOR2>(v);
+  v += dpp_mov<MOE_DPP_HMIRROR>(v);
+  v += dpp_mov<MOE_DPP_MIRROR>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
-  return v;
+  v = fmaxf(v, dpp_mov<MOE_DPP_XOR1>(v));
+  v = fmaxf(v, dpp_mov<MOE_DPP_XOR2>(v));
+  v = fmaxf(v, dpp_mov<MOE_DPP_HMIRROR>(v));
+  v = fmaxf(v, dpp_mov<MOE_DPP_MIRROR>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 __device__ inline int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
@@ -206,6 +234,10 @@ struct GemmParams {
   // t mod (gridDim.x * gridDim.y). null: none
   void* zero_y;
   int zero_T, zero_esz, zero_N;
+  // optional: the launch's work-groups also zero zero_n16 16-byte words at
+  // zero_ws (spread over them the same way). null: none
+  void* zero_ws;
+  int zero_n16;
   // host only: every expert weight tile is read by at most two work-groups
   // (segments of at most two row tiles), so the launch picks the variant that
   // streams the expert weights with non-temporal loads

@@ -105,6 +105,179 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
     slot_token[s] = -1;
 }
 
+// -------------------------------------------------------------------- one-launch path
+// Softmax / top-k, ranking, the scan over blocks, scatter and the tile lists of
+// a batch of more than one block of assignments in one launch. Block roles, in
+// the order the dispatcher starts them:
+//   [0, nsoft)             one wave per token: softmax / top-k as
+//                          softmax_topk_kernel; choice j of token t is then
+//                          published as keys[j * T + t] = expert + 1;
+//   [nsoft, nsoft + nblk)  ranker r: assignments r * DISP_BLOCK ... as the
+//                          count kernel, publishes its per-expert counts + 1 as
+//                          hist[r * E + e], adds up every ranker's counts (its
+//                          base and the totals), then scatters as the scatter
+//                          kernel;
+//   the last nplan         the tile lists (and offsets) from the totals.
+// A published word is written and read by agent-scope atomics (written through
+// to memory, read past the XCD's L2); 0, left by the launch before, means not
+// yet written. Softmax blocks wait for nothing and rankers publish before they
+// wait, so once the rankers and list builders (at most ROUTE_MAX_BLOCKS + a
+// few) are resident every wait ends. A wait that outlasts ROUTE_WAIT_TICKS gives
+// up: a key counts as no expert (the ranker publishes what it used, so every
+// block still sees the same counts), a count as 0. A block that gave up on a
+// count writes only in-range values (its tokens, slots < R_max) and leaves
+// slot_token's tail of -1 to the others; the offsets and the lists come from
+// one block, so they agree with each other, and every slot_token entry they
+// cover holds a token (the launch before zeroed them).
+#define ROUTE_WAIT_TICKS 5000000ull   // 50 ms of the 100 MHz real-time counter
+#define ROUTE_MAX_BLOCKS 64
+
+__device__ inline int pub_load(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline void pub_store(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// The published word at p, given its first read v; 0 if the wait gives up
+// (ok then false; later waits of the thread give up at once).
+__device__ inline int pub_wait(const int* p, int v, unsigned long long t0, bool& ok) {
+  while (v == 0) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > ROUTE_WAIT_TICKS) {
+      ok = false;
+      return 0;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = pub_load(p);
+  }
+  return v;
+}
+
+// One lane polls the word at p (sleeping between reads) before the block reads
+// all of its words: a hint, so that a block started early does not flood memory
+// with reads; the per-word waits that follow decide.
+__device__ inline void pub_hint(const int* p, unsigned long long t0) {
+  if (threadIdx.x == 0) {
+    while (pub_load(p) == 0 && __builtin_amdgcn_s_memrealtime() - t0 <= ROUTE_WAIT_TICKS)
+      __builtin_amdgcn_s_sleep(4);
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(DISP_BLOCK) void route_dispatch_kernel(RouteDispatchArgs a, int nsoft, int nblk,
+                                                                    int nplan, TilePlanArgs plan) {
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  if (b < nsoft) {
+    const int t = b * DISP_WAVES + tid / MOE_WAVE;
+    if (t >= a.T) return;
+    int sel[2];
+    wave_softmax_topk(a.z + (long long)t * a.E, a.E, a.k, a.renorm != 0,
+                      a.probs ? a.probs + (long long)t * a.E : nullptr, a.idx + (long long)t * a.k,
+                      a.topk_w + (long long)t * a.k, sel, a.zsplit, (long long)a.T * a.E);
+    if (lane_id() == 0)
+      for (int j = 0; j < a.k; ++j) pub_store(a.keys + (long long)j * a.T + t, sel[j] + 1);
+    return;
+  }
+  extern __shared__ int sh[];
+  const int E = a.E;
+  const bool ranker = b < nsoft + nblk;
+  const int rb = ranker ? b - nsoft : nblk;   // list builders count every ranker as earlier
+  int* wcnt = sh;                             // DISP_WAVES * (E + 1)
+  int* tot = wcnt + DISP_WAVES * (E + 1);     // E
+  int* sbase = tot + E;                       // E: counts of the earlier rankers
+  int* stot = sbase + E;                      // E: every ranker's counts
+  int* soff = stot + E;                       // E_loc + 1 (<= E + 1)
+  int* ssc = soff + E + 1;                    // DISP_WAVES + 1
+  int* plds = ssc + DISP_WAVES + 1;           // tile_plan_lds_ints(DISP_BLOCK)
+  __shared__ int full;                        // every count this block waited for came
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  const int kT = a.T * a.k;
+  const int as = rb * DISP_BLOCK + tid;
+  int key = E, r = -1;
+  if (ranker) {
+    pub_hint(a.keys + min(rb * DISP_BLOCK + DISP_BLOCK, kT) - 1, t0);
+    if (as < kT) {
+      bool kok = true;
+      const int* kp = a.keys + as;
+      const int v = pub_wait(kp, pub_load(kp), t0, kok);
+      key = (v >= 1 && v <= E) ? v - 1 : E;
+    }
+    r = block_rank<DISP_BLOCK>(key, E, wcnt, tot);
+    for (int e = tid; e < E; e += DISP_BLOCK) pub_store(a.hist + (long long)rb * E + e, tot[e] + 1);
+  } else {
+    pub_hint(a.hist + (long long)nblk * E - 1, t0);
+  }
+  if (tid == 0) full = 1;
+  __syncthreads();
+
+  // every ranker's counts: thread (e, j) of the tpe threads of expert e (adjacent
+  // lanes) adds rankers j, j + tpe, ..., four reads in flight at a time
+  int tpe = 1;
+  while (tpe < MOE_WAVE && E * tpe * 2 <= DISP_BLOCK) tpe *= 2;
+  const int e = tid / tpe, jj = tid - (tid / tpe) * tpe;
+  bool ok = true;
+  int before = 0, total = 0;
+  if (e < E) {
+    for (int b0 = jj; b0 < nblk; b0 += 4 * tpe) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int b2 = b0 + u * tpe;
+        v[u] = b2 < nblk ? pub_load(a.hist + (long long)b2 * E + e) : 1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int b2 = b0 + u * tpe;
+        if (b2 < nblk) {
+          const int c = pub_wait(a.hist + (long long)b2 * E + e, v[u], t0, ok);
+          const int cnt = c > 0 ? c - 1 : 0;
+          total += cnt;
+          if (b2 < rb) before += cnt;
+        }
+      }
+    }
+  }
+  for (int o = 1; o < tpe; o <<= 1) {
+    before += __shfl_xor(before, o, MOE_WAVE);
+    total += __shfl_xor(total, o, MOE_WAVE);
+  }
+  if (e < E && jj == 0) {
+    sbase[e] = before;
+    stot[e] = total;
+  }
+  if (!ok) full = 0;
+  __syncthreads();
+
+  const int kept = (tid < a.E_loc) ? min(stot[a.e_lo + tid], a.C) : 0;
+  int R;
+  const int off = block_excl_scan<DISP_BLOCK>(kept, ssc, &R);
+  if (nplan > 0 ? b == nsoft + nblk : rb == 0) {
+    for (int x = tid; x < E; x += DISP_BLOCK) a.demand[x] = stot[x];
+    if (tid < a.E_loc) a.offsets[tid] = off;
+    if (tid == 0) a.offsets[a.E_loc] = R;
+  }
+  if (!ranker) {
+    tile_plan_body<DISP_BLOCK>(kept, a.E_loc, plan, plds, b - nsoft - nblk, nplan);
+    return;
+  }
+  if (tid < a.E_loc) soff[tid] = off;
+  __syncthreads();
+  if (as < kT) {
+    const int j = as / a.T;
+    const int t = as - j * a.T;
+    int slot = -1;
+    if (key < E && key >= a.e_lo && key < a.e_lo + a.E_loc) {
+      const int pos = sbase[key] + r;
+      const int s2 = soff[key - a.e_lo] + pos;
+      if (pos < a.C && s2 < a.R_max) {   // (s2 < R_max always holds once every count came)
+        slot = s2;
+        a.slot_token[slot] = t;
+      }
+    }
+    a.token_slot[(long long)t * a.k + j] = slot;
+    if (a.y_zero && slot < 0) zero_dropped(a.y_zero, a.y_esz, t, a.H);
+  }
+  if (full)
+    for (int s = R + rb * DISP_BLOCK + tid; s < a.R_max; s += nblk * DISP_BLOCK) a.slot_token[s] = -1;
+}
+
 // -------------------------------------------------------------------- one-block path
 // Whole dispatch for k*T <= NTH in one block of NTH threads. MODE 0: the routing
 // comes from idx; MODE 1: softmax / top-k of every token first, from logits z
@@ -260,6 +433,28 @@ hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, 
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk + nplan), dim3(DISP_BLOCK), 0, s, idx, rank, blk_hist, T,
                      k, E, e_lo, E_loc, C, offsets, R_max, slot_token, token_slot, y_zero, y_esz, H, nblk, nplan,
                      pl);
+  return hipGetLastError();
+}
+
+bool route_dispatch_supported(long long kT) {
+  return kT > DISP_BLOCK && kT <= (long long)ROUTE_MAX_BLOCKS * DISP_BLOCK;
+}
+
+size_t route_dispatch_lds(int E) {
+  return sizeof(int) * ((size_t)DISP_WAVES * (E + 1) + 4 * (size_t)E + 1 + DISP_WAVES + 1 +
+                        tile_plan_lds_ints(DISP_BLOCK));
+}
+
+hipError_t launch_route_dispatch(const RouteDispatchArgs& a, const TilePlanArgs* plan, hipStream_t s) {
+  const long long kT = (long long)a.T * a.k;
+  if (!route_dispatch_supported(kT) || a.E < 1 || a.E > DISP_BLOCK || a.E_loc > a.E || a.k < 1 || a.k > 2)
+    return hipErrorInvalidValue;
+  const int nsoft = (a.T + DISP_WAVES - 1) / DISP_WAVES;
+  const int nblk = dispatch_num_blocks(kT);
+  const TilePlanArgs pl = plan_or_none(plan);
+  const int nplan = (pl.list1 || pl.list2) ? std::max(1, pl.parts) : 0;
+  hipLaunchKernelGGL(route_dispatch_kernel, dim3(nsoft + nblk + nplan), dim3(DISP_BLOCK), route_dispatch_lds(a.E),
+                     s, a, nsoft, nblk, nplan, pl);
   return hipGetLastError();
 }
 

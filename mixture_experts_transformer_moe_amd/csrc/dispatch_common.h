@@ -40,11 +40,14 @@ __device__ inline int block_rank(int key, int E, int* wcnt, int* tot) {
   if (rank_w == 0) wcnt[w * stride + key] = __popcll(m);
   __syncthreads();
   for (int e = tid; e < E; e += NTH) {
+    int c[NW];   // every wave's count read before the first write
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) c[ww] = wcnt[ww * stride + e];
     int run = 0;
+#pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      const int c = wcnt[ww * stride + e];
       wcnt[ww * stride + e] = run;
-      run += c;
+      run += c[ww];
     }
     tot[e] = run;
   }
@@ -67,8 +70,12 @@ __device__ inline int block_excl_scan(int v, int* sh /* NTH / 64 + 1 ints */, in
   if (lane == MOE_WAVE - 1) sh[w] = incl;
   __syncthreads();
   if (threadIdx.x == 0) {
+    int c[NW];   // every wave's total read before the first write
+#pragma unroll
+    for (int i = 0; i < NW; ++i) c[i] = sh[i];
     int run = 0;
-    for (int i = 0; i < NW; ++i) { int c = sh[i]; sh[i] = run; run += c; }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) { sh[i] = run; run += c[i]; }
     sh[NW] = run;
   }
   __syncthreads();

@@ -196,14 +196,21 @@ __device__ inline void fold_prefetch(const GemmParams& p, bool fold, int m0, int
 }
 
 // Zeroing of p.zero_y (the layer output, before a folded combine writes its
-// kept rows): work-group b of the launch (b = x + y * gridDim.x, over every K
-// slice) zeroes rows b, b + nb, ... after its K loop, in 16-byte stores.
+// kept rows) and of p.zero_ws (words a later launch publishes into): work-group
+// b of the launch (b = x + y * gridDim.x, over every K slice) zeroes rows b,
+// b + nb, ... and its share of the words after its K loop, in 16-byte stores.
 __device__ inline void zero_rows_share(const GemmParams& p) {
   const int nb = gridDim.x * gridDim.y, b = blockIdx.y * gridDim.x + blockIdx.x;
-  const int vecs = p.zero_N * p.zero_esz / 16;   // 16-byte vectors per row (N % 8 == 0)
-  for (int t = b; t < p.zero_T; t += nb) {
-    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.zero_y) + (long long)t * p.zero_N * p.zero_esz);
-    for (int c = threadIdx.x; c < vecs; c += blockDim.x) dst[c] = make_uint4(0u, 0u, 0u, 0u);
+  if (p.zero_y) {
+    const int vecs = p.zero_N * p.zero_esz / 16;   // 16-byte vectors per row (N % 8 == 0)
+    for (int t = b; t < p.zero_T; t += nb) {
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.zero_y) + (long long)t * p.zero_N * p.zero_esz);
+      for (int c = threadIdx.x; c < vecs; c += blockDim.x) dst[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if (p.zero_ws) {
+    uint4* dst = reinterpret_cast<uint4*>(p.zero_ws);
+    for (int c = b * blockDim.x + threadIdx.x; c < p.zero_n16; c += nb * blockDim.x) dst[c] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   // ---- which tile
   int seg, nt, mt, r0, r1;
   if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) {
-    if (p.zero_y) zero_rows_share(p);
+    if (p.zero_y || p.zero_ws) zero_rows_share(p);
     return;
   }
   const int m0 = r0 + mt * BM;        // first row-space row of the tile
@@ -514,7 +521,7 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #undef GEMM_LSTORE
 #undef GEMM_MATH
 #undef GEMM_SB
-  if (p.zero_y) zero_rows_share(p);
+  if (p.zero_y || p.zero_ws) zero_rows_share(p);
 
   if constexpr (std::is_same<BiasT, float>::value) {
     if (p.ksplit > 1) {   // partial sums of this slice; the bias goes with slice 0

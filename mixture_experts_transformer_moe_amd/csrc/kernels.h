@@ -34,6 +34,28 @@ hipError_t launch_dispatch_multi(const int* idx, int T, int k, int E, int e_lo, 
                                  hipStream_t s);
 hipError_t launch_gather_rows(int dtype, const void* x, const int* slot_token, int R_max, int H, void* xd,
                               hipStream_t s);
+// Softmax / top-k of every token, the whole dispatch and the tile lists in one
+// launch (more than one block of assignments). keys (k*T ints), hist (nblk*E
+// ints) and slot_token (R_max ints) must hold 0 at launch (the gate launch
+// before it zeroes them); z, zsplit and renorm as for launch_softmax_topk.
+struct RouteDispatchArgs {
+  const float* z;
+  int zsplit, renorm;
+  float* probs;   // nullable
+  float* topk_w;
+  int* idx;
+  int T, k, E, e_lo, E_loc, C, R_max, H, y_esz;
+  int* keys;
+  int* hist;
+  int* demand;
+  int* offsets;
+  int* slot_token;
+  int* token_slot;
+  void* y_zero;   // nullable, as for launch_dispatch_multi
+};
+bool route_dispatch_supported(long long kT);
+size_t route_dispatch_lds(int E);
+hipError_t launch_route_dispatch(const RouteDispatchArgs& a, const TilePlanArgs* plan, hipStream_t s);
 
 // gemm.hip
 enum { EPI_GELU = 0, EPI_F32 = 1 };

@@ -107,6 +107,7 @@ struct Plan {
   // dispatch
   bool disp_small;
   int nblk;
+  bool route_fused;  // softmax / top-k and the multi-block dispatch in one launch (words zeroed by the gate)
   // experts
   bool exp_decode;   // streaming kernels for segments of <= 8 rows, else grouped MFMA GEMM
   bool fold_combine; // top-1 standard layer: the second expert kernel (decode or grouped GEMM) writes y
@@ -228,6 +229,9 @@ moe_status_t validate_uncached(const moe_layer_desc_t* d, Plan* pl) {
   // one launch for both expert products: the vector-ALU gate kernel marks its h rows unwritten
   p.fused_decode = (d->flags & MOE_FLAG_DECODE_ONE_LAUNCH) && p.route_in_up && !p.gate_mfma &&
                    decode_fused_supported(p.dtype, p.H, p.F, p.exp_maxm);
+  // softmax / top-k and the whole multi-block dispatch in one launch, whose
+  // published words (keys, block counts) and slot_token the matrix-core gate zeroes
+  p.route_fused = !p.disp_small && !p.route_in_up && p.gate_mfma && route_dispatch_supported(kT);
   // matrix-core gate: each K step of a work-group waits on its loads, so a
   // short tile over all of K is latency-bound. Column tiles of 128 experts (x
   // read once per token tile); the tallest row tile and the fewest slices of K
@@ -408,7 +412,8 @@ moe_status_t check_weights(const Plan& p, const moe_layer_weights_t* w, bool exp
 // y_zero (matrix-core gate only): the layer output, zeroed by the gate's
 // work-groups before a folded top-1 combine writes its kept rows.
 moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, const float* gate_b, float* z,
-                             hipStream_t s, unsigned* fill = nullptr, int nfill = 0, void* y_zero = nullptr) {
+                             hipStream_t s, unsigned* fill = nullptr, int nfill = 0, void* y_zero = nullptr,
+                             void* ws_zero = nullptr, int ws_zero16 = 0) {
   if (p.gate_mfma) {
     GemmParams g{};
     if (y_zero) {
@@ -416,6 +421,10 @@ moe_status_t run_gate_logits(const Plan& p, const void* x, const void* gate_w, c
       g.zero_T = (int)p.T;
       g.zero_esz = (int)p.esz;
       g.zero_N = p.H;
+    }
+    if (ws_zero && ws_zero16 > 0) {
+      g.zero_ws = ws_zero;
+      g.zero_n16 = ws_zero16;
     }
     g.A = x;
     g.M = (int)p.T;
@@ -716,11 +725,12 @@ moe_status_t moe_layer_plan(const moe_layer_desc_t* d, moe_layer_plan_t* out) {
   out->tile_rows = p.exp_decode ? 0 : p.BM;
   out->tile_cols_w1 = p.exp_decode ? 0 : p.BN1;
   out->tile_cols_w2 = p.exp_decode ? 0 : p.BN2;
-  // gate; dispatch (one block, or softmax/top-k + count, scan, scatter); two
+  // gate; dispatch (one block, one launch of many blocks, or softmax/top-k +
+  // count, scan, scatter); two
   // expert kernels (the GEMMs' tile lists come from the dispatch); the dense
   // MLP's two unless inside the expert GEMMs; combine
   out->experts_one_launch = p.fused_decode ? 1 : 0;
-  out->launches = 1 + (p.route_in_up ? 0 : (p.disp_small ? 1 : 4)) + (p.fused_decode ? 1 : 2) +
+  out->launches = 1 + (p.route_in_up ? 0 : ((p.disp_small || p.route_fused) ? 1 : 4)) + (p.fused_decode ? 1 : 2) +
                   ((p.residual && !p.dense_in_experts && !p.dense_in_decode) ? 2 : 0) + (p.fold_combine ? 0 : 1);
   return MOE_OK;
 }
@@ -840,10 +850,15 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
 
   void* y_fold = p.fold_combine ? y : nullptr;
   ST_TRY(record(e.gate_begin, stream));
-  // the one-launch decode kernel finds its hidden rows marked unwritten (0xFFFF)
+  // the one-launch decode kernel finds its hidden rows marked unwritten (0xFFFF);
+  // the one-launch dispatch its keys, block counts and slot_token zeroed (one
+  // range: they lie back to back in the workspace, its end rounded up to 16
+  // bytes inside the alignment gap after slot_token)
+  const int zero16 =
+      p.route_fused ? (int)((p.o_slot_token + (size_t)p.R_max * 4 - p.o_rank + 15) / 16) : 0;
   ST_TRY(run_gate_logits(p, x, w->gate_w, w->gate_b, z, stream, p.fused_decode ? wsp<unsigned>(ws, p.o_h) : nullptr,
                          p.fused_decode ? (int)(p.R_max * p.F * (int64_t)p.esz / 4) : 0,
-                         p.zero_in_gate ? y : nullptr));
+                         p.zero_in_gate ? y : nullptr, p.route_fused ? wsp<char>(ws, p.o_rank) : nullptr, zero16));
   ST_TRY(record(e.gate_end, stream));
   ST_TRY(record(e.dispatch_begin, stream));
   RouteParams rp{};
@@ -869,8 +884,35 @@ moe_status_t moe_layer_forward_ex(const moe_layer_desc_t* d, const moe_layer_wei
   } else {
     // the GEMM path's tile lists come out of the dispatch kernel that finds the offsets
     const TilePlanArgs tp = tile_plan_args(p, ws, true);
-    ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot,
-                        p.zero_in_gate ? nullptr : y_fold, ws, stream, p.exp_decode ? nullptr : &tp));
+    if (p.route_fused) {
+      RouteDispatchArgs ra{};
+      ra.z = z;
+      ra.zsplit = p.gate_ksplit;
+      ra.renorm = p.renorm ? 1 : 0;
+      ra.probs = nullptr;
+      ra.topk_w = tw;
+      ra.idx = idx;
+      ra.T = (int)p.T;
+      ra.k = p.k;
+      ra.E = p.E;
+      ra.e_lo = p.e_lo;
+      ra.E_loc = p.E_loc;
+      ra.C = (int)std::min<int64_t>(p.C, INT32_MAX);
+      ra.R_max = (int)p.R_max;
+      ra.H = p.H;
+      ra.y_esz = (int)p.esz;
+      ra.keys = wsp<int>(ws, p.o_rank);
+      ra.hist = wsp<int>(ws, p.o_blk);
+      ra.demand = demand;
+      ra.offsets = offsets;
+      ra.slot_token = slot_token;
+      ra.token_slot = token_slot;
+      ra.y_zero = p.zero_in_gate ? nullptr : y_fold;
+      HIP_TRY(launch_route_dispatch(ra, p.exp_decode ? nullptr : &tp, stream), "softmax/top-k + dispatch");
+    } else {
+      ST_TRY(run_dispatch(p, true, z, nullptr, tw, idx, demand, offsets, slot_token, token_slot,
+                          p.zero_in_gate ? nullptr : y_fold, ws, stream, p.exp_decode ? nullptr : &tp));
+    }
   }
   ST_TRY(record(e.dispatch_end, stream));
   ST_TRY(record(e.ffn_begin, stream));

@@ -47,11 +47,14 @@ __device__ inline void tile_plan_body(int rows, int nseg, const TilePlanArgs& a,
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
   if (tid == 0) {
+    int t[NW];   // every wave's total read before the first write
+#pragma unroll
+    for (int i = 0; i < NW; ++i) t[i] = wsum[i];
     int run = 0;
+#pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const int t = wsum[i];
       wsum[i] = run;
-      run += t;
+      run += t[i];
     }
     wsum[NW] = run;
   }

@@ -105,15 +105,16 @@ def test_layer_plan_paths():
     """The plan names the path each benchmark layer takes and agrees with the
     sizing calls."""
     # launches: gate logits; the dispatch (none when the first expert kernel
-    # routes; else softmax/top-k + count, scan, scatter), whose single-block
-    # kernel also writes the GEMM tile lists; the two expert kernels; the dense
-    # MLP's two (none when its tiles join the expert GEMMs); the combine unless
-    # folded into the second expert kernel (every top-1 standard layer)
+    # routes; else one launch that also does softmax/top-k: one block, or many
+    # blocks after the matrix-core gate), which also writes the GEMM tile lists;
+    # the two expert kernels; the dense MLP's two (none when its tiles join the
+    # expert GEMMs); the combine unless folded into the second expert kernel
+    # (every top-1 standard layer)
     expect = {  # name: (gate, experts, dispatch in expert kernel, combine in expert kernel, launches)
         "decode_350m_moe128": ("vector", "stream", True, True, 1 + 0 + 2 + 0),
-        "prefill_1p3b_moe128": ("matrix", "grouped_gemm", False, True, 1 + 4 + 2 + 0),
-        "prmoe_residual": ("matrix", "grouped_gemm", False, False, 1 + 4 + 2 + 0 + 1),   # MLP inside the GEMMs
-        "share_24b_moe128": ("matrix", "grouped_gemm", False, False, 1 + 4 + 2 + 1),
+        "prefill_1p3b_moe128": ("matrix", "grouped_gemm", False, True, 1 + 1 + 2 + 0),
+        "prmoe_residual": ("matrix", "grouped_gemm", False, False, 1 + 1 + 2 + 0 + 1),   # MLP inside the GEMMs
+        "share_24b_moe128": ("matrix", "grouped_gemm", False, False, 1 + 1 + 2 + 1),
     }
     for name, (gate, experts, disp, comb, launches) in expect.items():
         shape = W.WORKLOADS[name]

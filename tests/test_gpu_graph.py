@@ -27,6 +27,10 @@ CASES = {
     "pingpong_160": W.LayerShape("graph_pp160", T=1024, H=512, F=1024, E=8, E_loc=8, k=2, cf=1.25, dtype="f16"),
     "pingpong_128_residual": W.LayerShape("graph_pp128", T=1024, H=512, F=1024, E=8, E_loc=8, k=1, cf=1.0,
                                           mlp_type="residual", dtype="bf16"),
+    # matrix-core gate (zeroing y and the dispatch's published words), then
+    # softmax / top-k and the multi-block dispatch in one launch, combine folded
+    "route_one_launch": W.LayerShape("graph_route", T=3000, H=256, F=512, E=64, E_loc=64, k=1, cf=1.25,
+                                     dtype="f16", zipf_s=1.1),
 }
 
 REPLAYS = 4

@@ -120,6 +120,21 @@ CASES = {
     # fp32 partial logits summed by the softmax / top-k, probabilities included
     "gate_k_slices": W.LayerShape("gks", T=512, H=2048, F=256, E=64, E_loc=8, e_lo=8, k=2, cf=1.0, dtype="f16"),
     "gate_k_slices_bf16": W.LayerShape("gksb", T=300, H=1024, F=256, E=128, E_loc=16, k=1, cf=1.0, dtype="bf16"),
+    # softmax / top-k and the multi-block dispatch in one launch (matrix-core
+    # gate, more than 1024 assignments): top-2 with a ragged last ranker block
+    "route_one_launch_k2": W.LayerShape("rk2", T=3000, H=256, F=512, E=64, E_loc=64, k=2, cf=1.0, dtype="f16"),
+    # ... a share of 16 of 128 Zipf-skewed experts, combine folded, bf16
+    "route_one_launch_share": W.LayerShape("rsh", T=2500, H=512, F=256, E=128, E_loc=16, e_lo=40, k=1, cf=1.25,
+                                           dtype="bf16", zipf_s=1.1),
+    # ... the gate's K in four slices (partial logits added in the launch)
+    "route_one_launch_kslices": W.LayerShape("rks", T=2100, H=2048, F=256, E=64, E_loc=64, k=1, cf=1.0, dtype="f16"),
+    # ... the most ranker blocks it takes (64 blocks of 1024 assignments)
+    "route_one_launch_64_blocks": W.LayerShape("r64", T=32768, H=64, F=128, E=64, E_loc=64, k=2, cf=1.0, dtype="f16"),
+    # ... a residual layer (the dense MLP's tiles in the tile lists it writes)
+    "route_one_launch_residual": W.LayerShape("rres", T=2048, H=256, F=512, E=64, E_loc=64, k=1, cf=2.0, dtype="f16",
+                                              mlp_type="residual"),
+    # ... feeding the streaming expert kernels (no tile lists: a ranker writes the offsets)
+    "route_one_launch_stream": W.LayerShape("rstr", T=1100, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
 }
 
 
