@@ -198,7 +198,9 @@ __device__ inline void fold_prefetch(const GemmParams& p, bool fold, int m0, int
 // Zeroing of p.zero_y (the layer output, before a folded combine writes its
 // kept rows) and of p.zero_ws (words a later launch publishes into): work-group
 // b of the launch (b = x + y * gridDim.x, over every K slice) zeroes rows b,
-// b + nb, ... and its share of the words after its K loop, in 16-byte stores.
+// b + nb, ... and its share of the words before its K loop, in 16-byte stores
+// that drain while the loop waits on its loads (prefill gate 14.5 -> 13.8 us
+// against zeroing after the loop).
 __device__ inline void zero_rows_share(const GemmParams& p) {
   const int nb = gridDim.x * gridDim.y, b = blockIdx.y * gridDim.x + blockIdx.x;
   if (p.zero_y) {
@@ -387,6 +389,7 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  if (p.zero_y || p.zero_ws) zero_rows_share(p);
   int nk = (int)(((long long)p.K * sizeof(T)) / 128);
   if constexpr (std::is_same<BiasT, float>::value) {
     if (p.ksplit > 1) {   // this work-group's slice of K (the host makes nk divisible)
@@ -521,7 +524,6 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #undef GEMM_LSTORE
 #undef GEMM_MATH
 #undef GEMM_SB
-  if (p.zero_y || p.zero_ws) zero_rows_share(p);
 
   if constexpr (std::is_same<BiasT, float>::value) {
     if (p.ksplit > 1) {   // partial sums of this slice; the bias goes with slice 0
