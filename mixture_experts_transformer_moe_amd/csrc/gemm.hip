@@ -39,6 +39,7 @@
 // segment's tiles spread evenly among them; the block index is remapped so
 // adjacent tiles land on the same XCD (work-groups are dealt round-robin over the
 // 8 XCDs) and share its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -315,8 +316,13 @@ __device__ inline bool gemm_tile(const GemmParams& p, int BM, int& seg, int& nt,
 // global loads in flight; the launch bound asks for two waves per SIMD when the
 // registers of two stages or of eight waves must fit. WNT: the expert tiles load
 // their weights non-temporally (the host sets it when every weight tile is read
-// by at most two row tiles).
-template <typename DT, int BM, int BN, int EPI, typename BiasT, int DEPTH, int NTH, bool WNT>
+// by at most two row tiles). PERS: a grid of resident work-groups walks the
+// tile list, work-group (x, j) on XCD x (x = blockIdx % 8) taking tiles j,
+// j + gridDim / 8, ... of XCD x's contiguous share of the list (the order
+// xcd_remap gives one tile per work-group); the residual layer's second GEMM,
+// whose list mixes the dense MLP's tiles with the experts', runs 443 -> 429 us
+// so, the other weight-streaming launches measured unchanged.
+template <typename DT, int BM, int BN, int EPI, typename BiasT, int DEPTH, int NTH, bool WNT, bool PERS = false>
 __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped_gemm_kernel(GemmParams p) {
   using T = typename DT::T;
   constexpr int NW = NTH / 64;
@@ -331,11 +337,37 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   constexpr int STAGE = (BN + BM) * LDS_ROW;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
+  int it_L = 0, it_end = 0, it_step = 1;   // PERS: this work-group's tiles it_L, it_L + it_step, ... < it_end
+  if constexpr (PERS) {
+    const int total = *p.tile_count * p.n_ntiles;
+    const int xcd = blockIdx.x & 7, g8 = gridDim.x >> 3;   // (the host launches a multiple of 8)
+    const int q = total >> 3, rr = total & 7;
+    const int start = xcd * q + min(xcd, rr);
+    it_L = start + (int)(blockIdx.x >> 3);
+    it_end = start + q + (xcd < rr ? 1 : 0);
+    it_step = g8;
+  }
+  for (;;) {
   // ---- which tile
   int seg, nt, mt, r0, r1;
-  if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) {
-    if (p.zero_y || p.zero_ws) zero_rows_share(p);
-    return;
+  if constexpr (PERS) {
+    if (it_L >= it_end) return;
+    const int2 d = p.tiles[it_L];
+    seg = d.x;
+    nt = d.y >> 16;
+    mt = d.y & 0xffff;
+    if (seg == p.nseg) {   // the extra segment
+      r0 = 0;
+      r1 = p.M2;
+    } else {
+      r0 = p.seg_off[seg];
+      r1 = p.seg_off[seg + 1];
+    }
+  } else {
+    if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) {
+      if (p.zero_y || p.zero_ws) zero_rows_share(p);
+      return;
+    }
   }
   const int m0 = r0 + mt * BM;        // first row-space row of the tile
   const bool extra = seg == p.nseg;   // the extra segment: its own operands, rows index A2 directly
@@ -389,7 +421,9 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (p.zero_y || p.zero_ws) zero_rows_share(p);
+  if constexpr (!PERS) {
+    if (p.zero_y || p.zero_ws) zero_rows_share(p);
+  }
   int nk = (int)(((long long)p.K * sizeof(T)) / 128);
   if constexpr (std::is_same<BiasT, float>::value) {
     if (p.ksplit > 1) {   // this work-group's slice of K (the host makes nk divisible)
@@ -537,6 +571,10 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   }
   gemm_epilogue<DT, EPI, BiasT, TN, TM>(p, acc, seg, nt * BN + wave_n * TN * 16, m0 + wave_m * TM * 16, r1, lane, ftok,
                                         fw);
+  if constexpr (!PERS) return;
+  it_L += it_step;
+  __syncthreads();   // (every wave's last fragment reads are done before the next tile's LDS stores)
+  }
 }
 
 
@@ -929,10 +967,33 @@ struct LaunchEv {
   hipEvent_t start, stop;
 };
 
-// Four-wave tiles keep two stages of loads in flight for tiles of <= 64 rows
-// (weight streaming, the register budget allows it), one for 128 x 128 (more
-// reuse per byte, and two would cost occupancy). 256-column tiles run in the
-// eight-wave ping-pong kernel.
+// Work-groups of a kernel resident on the whole device at once, from its
+// registers and LDS and gfx950's limits (512 registers per lane of a SIMD in
+// granules of 8, at most 8 waves per SIMD, 4 SIMDs and 160 KB of LDS per CU),
+// rounded down to a multiple of 8; cached per kernel and device; 0 if unknown.
+template <auto KERNEL>
+static int resident_workgroups(int nth) {
+  static int cache[64];   // per device (one array per kernel: KERNEL is a template argument)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    hipFuncAttributes fa;
+    int cus = 0;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(KERNEL)) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || fa.numRegs <= 0 ||
+        cus < 1)
+      return 0;
+    const int regs = (fa.numRegs + 7) / 8 * 8;
+    const int waves_simd = std::min(8, 512 / regs);
+    const int by_waves = waves_simd * 4 / ((nth + 63) / 64);
+    const int by_lds = fa.sharedSizeBytes > 0 ? (int)((160 * 1024) / fa.sharedSizeBytes) : 64;
+    const int per_cu = std::min(by_waves, by_lds);
+    if (per_cu < 1) return 0;
+    cache[dev] = per_cu * cus / 8 * 8;
+  }
+  return cache[dev];
+}
+
 template <typename DT, int BM, int BN, int EPI, typename BiasT>
 static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) {
   constexpr int NTH = BN == 256 ? 512 : GEMM_THREADS;
@@ -958,6 +1019,17 @@ static void launch_t(const GemmParams& p, int grid, hipStream_t s, LaunchEv ev) 
     // (float bias: the gate's logits, whose weight tile every token tile reads)
     if constexpr (!std::is_same<BiasT, float>::value) {
       if (p.stream_w) {   // expert weights read by one or two row tiles each
+        if constexpr (DEPTH == 2 && NTH == 256) {
+          if (p.tiles && p.ksplit <= 1) {   // resident work-groups walking the tile list
+            constexpr auto kern = grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, true, true>;
+            const int slots = resident_workgroups<kern>(NTH);
+            if (slots >= 8) {
+              const int gp = grid < slots ? (grid + 7) / 8 * 8 : slots;
+              MOE_LAUNCH(kern, dim3(gp), dim3(NTH), 0, s, ev.start, ev.stop, p);
+              return;
+            }
+          }
+        }
         MOE_LAUNCH((grouped_gemm_kernel<DT, BM, BN, EPI, BiasT, DEPTH, NTH, true>), g, dim3(NTH), 0, s, ev.start,
                    ev.stop, p);
         return;
