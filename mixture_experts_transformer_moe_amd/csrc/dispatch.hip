@@ -124,11 +124,13 @@ __global__ __launch_bounds__(DISP_BLOCK) void dispatch_scatter_kernel(
 // wait, so once the rankers and list builders (at most ROUTE_MAX_BLOCKS + a
 // few) are resident every wait ends. A wait that outlasts ROUTE_WAIT_TICKS gives
 // up: a key counts as no expert (the ranker publishes what it used, so every
-// block still sees the same counts), a count as 0. A block that gave up on a
-// count writes only in-range values (its tokens, slots < R_max) and leaves
-// slot_token's tail of -1 to the others; the offsets and the lists come from
-// one block, so they agree with each other, and every slot_token entry they
-// cover holds a token (the launch before zeroed them).
+// block still sees the same counts), a count as 0. Blocks that gave up on a
+// count may then disagree, but each writes only in-range values (its tokens,
+// slots < R_max, offsets <= R_max) and leaves slot_token's tail of -1 to the
+// others; every slot_token entry below the offsets' end holds a token (the
+// launch before zeroed them), and the GEMMs skip any list entry that names no
+// tile with rows under the offsets (tile_entry), so nothing downstream reads or
+// writes out of bounds.
 #define ROUTE_WAIT_TICKS 5000000ull   // 50 ms of the 100 MHz real-time counter
 #define ROUTE_MAX_BLOCKS 64
 

@@ -283,25 +283,37 @@ __device__ inline void gemm_epilogue_lds(const GemmParams& p, const float4_t (&a
   }
 }
 
+// Entry L of the tile list: (segment, column tile, row tile) and the segment's
+// row range. False for an entry that names no tile with rows (a segment or
+// column tile out of range, or rows past the segment's end), which the caller
+// skips: the lists the dispatch writes hold none, and with this check no entry
+// can send a work-group outside its operands.
+__device__ inline bool tile_entry(const GemmParams& p, int BM, int L, int& seg, int& nt, int& mt, int& r0, int& r1) {
+  const int2 d = p.tiles[L];
+  seg = d.x;
+  nt = d.y >> 16;
+  mt = d.y & 0xffff;
+  if ((unsigned)seg > (unsigned)p.nseg || nt >= p.n_ntiles) return false;
+  if (seg == p.nseg) {       // the extra segment
+    r0 = 0;
+    r1 = p.M2;
+  } else {
+    r0 = p.seg_off[seg];
+    r1 = p.seg_off[seg + 1];
+  }
+  return r0 >= 0 && r0 + mt * BM < r1;
+}
+
 // Which output tile a work-group computes: (segment, column tile, row tile) and
-// the segment's row range. Returns false past the end of the tile list.
+// the segment's row range. Returns false past the end of the tile list (or for
+// an entry tile_entry rejects).
 __device__ inline bool gemm_tile(const GemmParams& p, int BM, int& seg, int& nt, int& mt, int& r0, int& r1) {
   const int nmt = p.tiles ? *p.tile_count : (p.M + BM - 1) / BM;
   const int total = nmt * p.n_ntiles;
   if ((int)blockIdx.x >= total) return false;
   const int L = xcd_remap(blockIdx.x, total);
   if (p.tiles) {
-    const int2 d = p.tiles[L];
-    seg = d.x;
-    nt = d.y >> 16;
-    mt = d.y & 0xffff;
-    if (seg == p.nseg) {       // the extra segment
-      r0 = 0;
-      r1 = p.M2;
-    } else {
-      r0 = p.seg_off[seg];
-      r1 = p.seg_off[seg + 1];
-    }
+    if (!tile_entry(p, BM, L, seg, nt, mt, r0, r1)) return false;
   } else {
     seg = 0;
     nt = L / nmt;
@@ -352,16 +364,9 @@ __global__ __launch_bounds__(NTH, (DEPTH > 1 || NTH > 256) ? 2 : 1) void grouped
   int seg, nt, mt, r0, r1;
   if constexpr (PERS) {
     if (it_L >= it_end) return;
-    const int2 d = p.tiles[it_L];
-    seg = d.x;
-    nt = d.y >> 16;
-    mt = d.y & 0xffff;
-    if (seg == p.nseg) {   // the extra segment
-      r0 = 0;
-      r1 = p.M2;
-    } else {
-      r0 = p.seg_off[seg];
-      r1 = p.seg_off[seg + 1];
+    if (!tile_entry(p, BM, it_L, seg, nt, mt, r0, r1)) {
+      it_L += it_step;
+      continue;
     }
   } else {
     if (!gemm_tile(p, BM, seg, nt, mt, r0, r1)) {
