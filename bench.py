@@ -206,7 +206,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the layer on one GPU's expert share "
+        print("bench.py measures one GPU only: the library runs the layer on one GPU's expert share "
               "(no collectives); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
