@@ -135,6 +135,10 @@ CASES = {
                                               mlp_type="residual"),
     # ... feeding the streaming expert kernels (no tile lists: a ranker writes the offsets)
     "route_one_launch_stream": W.LayerShape("rstr", T=1100, H=512, F=512, E=256, E_loc=256, k=1, cf=1.0, dtype="f16"),
+    # ... two ranker blocks, the second holding one assignment
+    "route_one_launch_1025": W.LayerShape("r1025", T=1025, H=256, F=512, E=64, E_loc=64, k=1, cf=1.0, dtype="f16"),
+    # ... the largest expert count (two threads per expert add the block counts)
+    "route_one_launch_e512": W.LayerShape("r512", T=1500, H=256, F=512, E=512, E_loc=512, k=1, cf=4.0, dtype="f16"),
 }
 
 
