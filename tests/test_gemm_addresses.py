@@ -1,4 +1,5 @@
-"""Address bounds of the ping-pong grouped GEMM's direct-to-LDS loads (CPU only).
+"""Address bounds of the ping-pong grouped GEMM's direct-to-LDS loads, and the
+tile walk of the persistent weight-streaming launches (CPU only).
 
 The eight-wave 128 / 256 / 320 x 256 tiles load each K step through two buffer
 descriptors without range checks: the weight descriptor starts at the tile's
@@ -122,3 +123,38 @@ def test_plan_picks_320_rows_for_short_batches():
     inside x."""
     plan = B.moe_layer_plan(B.make_desc(150, 256, 512, 2, 2, 2.0, "f16"))
     assert plan["tile"] == (320, 256, 256)
+
+
+def persistent_walk(total, grid):
+    """Tiles each work-group of a persistent weight-streaming launch takes, as the
+    kernel computes them: work-group b runs on XCD x = b % 8 and takes tiles
+    start_x + b // 8, + grid // 8, ... below end_x, where [start_x, end_x) is XCD
+    x's contiguous share of the list (the split one tile per work-group gives)."""
+    g8 = grid // 8
+    q, rr = total // 8, total % 8
+    walks = []
+    for b in range(grid):
+        x, j = b % 8, b // 8
+        start = x * q + min(x, rr)
+        end = start + q + (1 if x < rr else 0)
+        walks.append(list(range(start + j, end, g8)))
+    return walks
+
+
+def xcd_remap(i, total):
+    q, r = total // 8, total % 8
+    x, slot = i % 8, i // 8
+    return x * q + min(x, r) + slot
+
+
+@pytest.mark.parametrize("grid", [8, 512, 768, 1024])
+def test_persistent_walk_covers_every_tile_once(grid):
+    """Every tile of the list is taken by exactly one work-group, by one on the
+    XCD that the one-tile-per-work-group launch would give it."""
+    for total in list(range(0, 80)) + [527, 528, 1055, 1056, 2112, 6144, 65535]:
+        walks = persistent_walk(total, grid)
+        taken = sorted(t for w in walks for t in w)
+        assert taken == list(range(total)), (total, grid)
+        one_per_wg = {xcd_remap(i, total): i % 8 for i in range(total)}
+        for b, w in enumerate(walks):
+            assert all(one_per_wg[t] == b % 8 for t in w), (total, grid, b)
