@@ -126,6 +126,28 @@ __device__ inline float wave_max(float v) {
 
 __device__ inline int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
 
+// v of lane (lane ^ O): DPP moves inside rows of 16 lanes for O < 16 (xor 1 and
+// 2 by quad permutes, xor 8 by a rotate of the row by 8, xor 4 by a rotate by 12
+// (lanes with bit 2 clear, taking lane + 4) or by 4 (the others, lane - 4)), a
+// bpermute shuffle across rows. The same values as __shfl_xor, without the LDS
+// round trip inside a row. Every lane of the wave must be active.
+template <int O>
+__device__ inline float shfl_xor_wave(float v, int lane) {
+  if constexpr (O == 1) {
+    return dpp_mov<MOE_DPP_XOR1>(v);
+  } else if constexpr (O == 2) {
+    return dpp_mov<MOE_DPP_XOR2>(v);
+  } else if constexpr (O == 4) {
+    const float up = dpp_mov<0x12C>(v);   // row_ror:12: lane i takes lane (i + 4) mod 16
+    const float dn = dpp_mov<0x124>(v);   // row_ror:4: lane i takes lane (i - 4) mod 16
+    return (lane & 4) ? dn : up;
+  } else if constexpr (O == 8) {
+    return dpp_mov<0x128>(v);             // row_ror:8: lane i takes lane i ^ 8
+  } else {
+    return __shfl_xor(v, O, 64);
+  }
+}
+
 // Reduce N per-lane values over the whole wave at once (N a power of two, <= 64).
 // Transpose steps: at offset O each lane pair swaps half of its values, so after
 // log2(N) steps lane l holds one index, l >> (6 - log2 N), summed over the lanes
@@ -141,7 +163,7 @@ struct WaveTranspose {
     for (int j = 0; j < h; ++j) {
       const float send = hi ? v[j] : v[j + h];
       const float keep = hi ? v[j + h] : v[j];
-      v[j] = keep + __shfl_xor(send, O, 64);
+      v[j] = keep + shfl_xor_wave<O>(send, lane);
     }
     WaveTranspose<h, O / 2>::run(v, lane);
   }
@@ -158,8 +180,12 @@ __device__ inline float wave_reduce_multi(float (&v)[N]) {
   const int lane = threadIdx.x & 63;
   WaveTranspose<N, 32>::run(v, lane);
   float r = v[0];
-#pragma unroll
-  for (int o = 32 / N; o >= 1; o >>= 1) r += __shfl_xor(r, o, 64);
+  if constexpr (32 / N >= 32) r += shfl_xor_wave<32>(r, lane);
+  if constexpr (32 / N >= 16) r += shfl_xor_wave<16>(r, lane);
+  if constexpr (32 / N >= 8) r += shfl_xor_wave<8>(r, lane);
+  if constexpr (32 / N >= 4) r += shfl_xor_wave<4>(r, lane);
+  if constexpr (32 / N >= 2) r += shfl_xor_wave<2>(r, lane);
+  if constexpr (32 / N >= 1) r += shfl_xor_wave<1>(r, lane);
   return r;
 }
 

@@ -49,8 +49,8 @@ __device__ inline bool find_active(const int* __restrict__ seg_off, int nseg, in
       const uint64_t pick = __ballot(ne && __popcll(below) == g - base);
       const int src = __ffsll((unsigned long long)pick) - 1;
       seg = i * 64 + src;
-      r0 = __shfl(lo[i], src, 64);
-      r1 = __shfl(hi[i], src, 64);
+      r0 = __builtin_amdgcn_readlane(lo[i], src);   // (src is the same in every lane)
+      r1 = __builtin_amdgcn_readlane(hi[i], src);
       return true;
     }
     base += cnt;
