@@ -128,9 +128,10 @@ __device__ inline int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
 
 // v of lane (lane ^ O): DPP moves inside rows of 16 lanes for O < 16 (xor 1 and
 // 2 by quad permutes, xor 8 by a rotate of the row by 8, xor 4 by a rotate by 12
-// (lanes with bit 2 clear, taking lane + 4) or by 4 (the others, lane - 4)), a
-// bpermute shuffle across rows. The same values as __shfl_xor, without the LDS
-// round trip inside a row. Every lane of the wave must be active.
+// (lanes with bit 2 clear, taking lane + 4) or by 4 (the others, lane - 4));
+// gfx950's lane-swap instructions for 16 and 32 (a swap of v with itself leaves
+// each lane's partner value in one of its two results). The same values as
+// __shfl_xor, with no LDS round trip. Every lane of the wave must be active.
 template <int O>
 __device__ inline float shfl_xor_wave(float v, int lane) {
   if constexpr (O == 1) {
@@ -143,8 +144,17 @@ __device__ inline float shfl_xor_wave(float v, int lane) {
     return (lane & 4) ? dn : up;
   } else if constexpr (O == 8) {
     return dpp_mov<0x128>(v);             // row_ror:8: lane i takes lane i ^ 8
+  } else if constexpr (O == 16) {
+    // [0]: lanes 16-31 / 48-63 hold lanes 0-15 / 32-47; [1]: lanes 0-15 / 32-47 hold 16-31 / 48-63
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (lane & 16) ? r[0] : r[1]);
   } else {
-    return __shfl_xor(v, O, 64);
+    static_assert(O == 32, "xor 1, 2, 4, 8, 16 or 32");
+    // [0]: lanes 32-63 hold lanes 0-31; [1]: lanes 0-31 hold lanes 32-63
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
   }
 }
 
