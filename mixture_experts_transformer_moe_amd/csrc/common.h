@@ -158,6 +158,20 @@ __device__ inline float shfl_xor_wave(float v, int lane) {
   }
 }
 
+// Inclusive sum of v over lanes 0 .. lane (integers, so exact in any order):
+// DPP row shifts by 1, 2, 4 and 8 scan each row of 16 lanes (a lane with no
+// source adds 0), then the row broadcasts add lane 15's total to rows 1 and 3
+// and lane 31's to rows 2 and 3. Every lane of the wave must be active.
+__device__ inline int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2 and 3
+  return v;
+}
+
 // Reduce N per-lane values over the whole wave at once (N a power of two, <= 64).
 // Transpose steps: at offset O each lane pair swaps half of its values, so after
 // log2(N) steps lane l holds one index, l >> (6 - log2 N), summed over the lanes

@@ -61,12 +61,7 @@ __device__ inline int block_excl_scan(int v, int* sh /* NTH / 64 + 1 ints */, in
   constexpr int NW = NTH / MOE_WAVE;
   const int lane = lane_id();
   const int w = threadIdx.x / MOE_WAVE;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < MOE_WAVE; o <<= 1) {
-    int u = __shfl_up(incl, o, MOE_WAVE);
-    if (lane >= o) incl += u;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == MOE_WAVE - 1) sh[w] = incl;
   __syncthreads();
   if (threadIdx.x == 0) {

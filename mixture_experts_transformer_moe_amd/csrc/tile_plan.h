@@ -38,12 +38,7 @@ __device__ inline void tile_plan_body(int rows, int nseg, const TilePlanArgs& a,
   const int lane = tid & 63, w = tid >> 6;
   const int c = (tid < nseg) ? (rows + a.BM - 1) / a.BM : 0;
   C[tid] = c;
-  int incl = c;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  const int incl = wave_incl_scan(c);
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
   if (tid == 0) {
